@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the 1-bit Adam compression-phase step on one MI355X.
+
+A step is one ob_adam_compressed_step over one batch of n workers' synthetic
+gradients (all of the compressed step: worker compress, worker scales,
+server average/re-compress, server scales, decompress + frozen-variance
+update).  Default workload: d = 110,000,128 fp32 parameters (a BERT-Base
+sized flat vector), n = 8 simulated workers, bf16 gradients N(0, 1e-3),
+2 full-precision warm-up steps before the compressed ones.  All gradient
+batches are generated on the GPU before the timed region.
+
+Prints one JSON line: params*workers/s of the whole step, the worker pass's
+roofline against MI355X's 8 TB/s HBM peak (timed live with HIP events the
+library records on its stream), and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "compressed-step params·workers/sec and achieved HBM GB/s (% of peak), 1 GPU"
+KERNEL_SRC = os.path.join(ROOT, "communication_compressed_distributed_02_amd", "csrc",
+                          "ob_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_worker_pass_c2.json")
+
+
+def alg_bytes(w):
+    """Algorithmic HBM bytes per kernel launch of one steady-state compressed
+    step (momentum held as server sign words + scales; every array touched
+    once; partials of the fixed-order sums included)."""
+    d, n = w.d, w.n
+    gb = 2 if w.bf16 else 4
+    nseg = -(-w.L // 1024)
+    part_w = 8 * n * n * nseg
+    part_s = 8 * n * nseg
+    return {
+        # grad in, compensated momentum in and out, sign words out, momentum words in
+        "worker": n * d * (gb + 4 + 4) + n * d // 8 + d // 8 + part_w,
+        "worker_scale": part_w + 4 * n * n,
+        # worker sign words in, server u in and out, server words out
+        "server": n * d // 8 + 8 * d + d // 8 + part_s + 4 * n * n,
+        "server_scale": part_s + 4 * n,
+        # server words in, x in and out, v in
+        "update": d // 8 + 12 * d + 4 * n,
+    }
+
+
+def survey_b_alg(w):
+    """Bytes per step with the momentum kept in fp32 (read and written each
+    step) and the server-bit read counted per worker: d*[n*(gb+8.25)+28.125]."""
+    gb = 2 if w.bf16 else 4
+    return w.d * (w.n * (gb + 8.25) + 28.125)
+
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """Counter-measured HBM bytes per worker-pass launch, if they were taken
+    on the current kernel source (else None)."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_sha() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, steps=1):
+    """The CPU oracle on chunk 0 (all n workers, 1/n of the step's work),
+    timed over `steps` compressed steps after the warm-up, scaled by n."""
+    import oracle
+    from synth import workloads as W
+    L = w.L
+    o = oracle.Oracle(w.d, w.n, w.beta1, w.beta2, w.eps, j0=0, j1=1, keep_debug=False)
+    secs = []
+    for t in range(w.warmup + steps):
+        g = [W.cpu_grad(w, i, t, 0, L) for i in range(w.n)]
+        if t < w.warmup:
+            o.warmup_step(g, w.lr_at(t))
+            continue
+        t0 = time.perf_counter()
+        o.compressed_step(g, w.lr_at(t))
+        secs.append(time.perf_counter() - t0)
+    o.close()
+    per_step = sum(secs) / len(secs) * w.n
+    return {"value": w.n * w.d / per_step, "unit": "params*workers/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "chunk 0 of %d (%d elements x %d workers), %d compressed step(s) after "
+                      "%d warm-up steps, single thread, time x%d for the whole step"
+                      % (w.n, L, w.n, steps, w.warmup, w.n),
+            "s_per_step_extrapolated": per_step}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3, help="untimed compressed steps")
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=1)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: the simulated workers live on one MI355X; "
+              "--gpus %d is not supported" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from communication_compressed_distributed_02_amd import ob_adam as ob
+    from synth import workloads as W
+
+    w = W.make(a.workload)
+    if w.staged:
+        raise SystemExit("bench.py times the all-workers entry point; %s is staged" % w.name)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gdt = torch.bfloat16 if w.bf16 else torch.float32
+    batches = w.warmup + a.warmup + a.steps
+    print("# generating %d gradient batches of %d x %d %s on the GPU"
+          % (batches, w.n, w.d, "bf16" if w.bf16 else "fp32"), file=sys.stderr, flush=True)
+    grads = []
+    for t in range(batches):
+        g = torch.empty((w.n, w.d), dtype=gdt, device=dev)
+        for i in range(w.n):
+            synth.fill_gpu(g[i], 0, t, i, w.dist, w.sigma)
+            for lo, hi in w.pads:
+                g[i, lo:hi].zero_()
+        grads.append(list(g.unbind(0)))
+    opt = ob.OneBitAdam(w.d, w.n, ob.OB_GRAD_BF16 if w.bf16 else ob.OB_GRAD_F32, w.beta1,
+                        w.beta2, w.eps, device=dev)
+    for t in range(w.warmup):
+        opt.warmup_step(grads[t], w.lr_at(t))
+    for t in range(w.warmup, w.warmup + a.warmup):
+        opt.compressed_step(grads[t], w.lr_at(t))
+    torch.cuda.synchronize()
+    print("# timing %d compressed steps" % a.steps, file=sys.stderr, flush=True)
+
+    ob.ob_adam_set_timing(opt.h, 5 * a.steps + 8)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(a.steps):
+        t = w.warmup + a.warmup + i
+        opt.compressed_step(grads[t], w.lr_at(t))
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / a.steps
+    kt, dropped = ob.ob_adam_kernel_times(opt.h)
+    ob.ob_adam_set_timing(opt.h, 0)
+
+    ab = alg_bytes(w)
+    kernels = {}
+    for k in ("worker", "worker_scale", "server", "server_scale", "update"):
+        ms, cnt = kt[k]
+        if cnt:
+            avg = ms / cnt
+            kernels[k] = {"avg_ms": round(avg, 5), "launches": cnt, "alg_bytes": ab[k],
+                          "GB_s": round(ab[k] / (avg * 1e-3) / 1e9, 1)}
+    wk = kernels["worker"]
+    traffic = load_traffic(w.name)
+    step_bytes = sum(ab.values())
+    result = {
+        "metric": METRIC,
+        "value": w.n * w.d / (ms_step * 1e-3),
+        "unit": "params*workers/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": dict(W.describe(w), parallelism="n simulated data-parallel workers on 1 GPU"),
+        "roofline": {"bound": "hbm", "kernel": "worker pass",
+                     "achieved": round(wk["GB_s"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(wk["GB_s"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "step": {"alg_bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                 "frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "fp32_momentum_bytes": survey_b_alg(w),
+                 "fp32_momentum_frac_of_peak": round(
+                     survey_b_alg(w) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "wall_s": round(wall, 4), "timing_launches_dropped": dropped},
+        "kernels": kernels,
+    }
+    del grads, opt
+    torch.cuda.empty_cache()
+    if not a.no_cpu_baseline:
+        print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, a.cpu_steps)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

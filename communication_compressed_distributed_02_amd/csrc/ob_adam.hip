@@ -1,0 +1,373 @@
+// Host side of the ob_adam C interface: validation, workspace carve-up,
+// phase rules and the launch sequence of a step.  See include/ob_adam.h for
+// the contract; the kernels are in ob_kernels.hip.
+#include "ob_adam.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <new>
+#include <vector>
+
+#include "ob_kernels.h"
+
+struct ob_adam_handle {
+  ob::State st;
+  hipStream_t stream;
+  int64_t steps;        // warm-up + compressed steps taken
+  int64_t compressed;   // compressed steps taken
+  int64_t warm;         // warm-up steps taken
+  bool staged_open;     // a worker-at-a-time step has started
+  uint64_t staged_mask; // workers already compressed in the open step
+  bool poisoned;
+  // per-kernel timing (events recorded around each launch when enabled)
+  std::vector<hipEvent_t> ev;          // 2 per timed launch
+  std::vector<int> ev_kernel;          // kernel id of each timed launch
+  int64_t ev_used = 0, ev_dropped = 0;
+};
+
+namespace {
+
+bool valid_beta(float b) { return isfinite(b) && b >= 0.0f && b < 1.0f; }
+
+ob_status check_config(const ob_adam_config* cfg) {
+  if (cfg == nullptr) return OB_ERR_ARG;
+  if (cfg->grad_dtype != OB_GRAD_F32 && cfg->grad_dtype != OB_GRAD_BF16) return OB_ERR_ARG;
+  if (!valid_beta(cfg->beta1) || !valid_beta(cfg->beta2) || !isfinite(cfg->eps) ||
+      cfg->eps < 0.0f)
+    return OB_ERR_ARG;
+  if (cfg->d <= 0 || cfg->n_workers < 1 || cfg->n_workers > ob::kMaxWorkersPerLaunch)
+    return OB_ERR_SHAPE;
+  if (cfg->d % (64 * (int64_t)cfg->n_workers) != 0) return OB_ERR_SHAPE;
+  const int64_t L = cfg->d / cfg->n_workers;
+  if ((L + ob::kSegElems - 1) / ob::kSegElems > ob::kMaxSegsPerChunk) return OB_ERR_SHAPE;
+  return OB_OK;
+}
+
+ob_status fail(ob_adam_t h, hipError_t e) {
+  if (e == hipSuccess) return OB_OK;
+  h->poisoned = true;
+  return OB_ERR_HIP;
+}
+
+ob_status usable(ob_adam_t h) {
+  if (h == nullptr) return OB_ERR_ARG;
+  if (h->poisoned) return OB_ERR_HIP;
+  return OB_OK;
+}
+
+// Launch `fn` bracketed by timing events when timing is on.
+template <typename F>
+hipError_t timed(ob_adam_t h, int kernel, F fn) {
+  const int64_t cap = (int64_t)h->ev_kernel.size();
+  if (cap == 0) return fn();
+  if (h->ev_used >= cap) {
+    h->ev_dropped += 1;
+    return fn();
+  }
+  const int64_t i = h->ev_used;
+  hipError_t e = hipEventRecord(h->ev[2 * i], h->stream);
+  if (e != hipSuccess) return e;
+  e = fn();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(h->ev[2 * i + 1], h->stream);
+  if (e != hipSuccess) return e;
+  h->ev_kernel[i] = kernel;
+  h->ev_used = i + 1;
+  return hipSuccess;
+}
+
+void release_events(ob_adam_t h) {
+  for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+  h->ev.clear();
+  h->ev_kernel.clear();
+  h->ev_used = 0;
+  h->ev_dropped = 0;
+}
+
+ob_status gather_grads(ob_adam_t h, const void* const* grads, int w0, int nw, ob::GradPtrs* g) {
+  if (grads == nullptr) return OB_ERR_ARG;
+  for (int i = 0; i < nw; ++i) {
+    if (grads[w0 + i] == nullptr) return OB_ERR_ARG;
+    g->p[i] = grads[w0 + i];
+  }
+  (void)h;
+  return OB_OK;
+}
+
+// Worker scales, server pass, server scales, update; then count the step.
+ob_status finish_step(ob_adam_t h, float lr) {
+  const ob::State& s = h->st;
+  hipStream_t st = h->stream;
+  hipError_t e = timed(h, OB_K_WORKER_SCALE, [&] { return ob::launch_worker_scales(s, st); });
+  if (e == hipSuccess) e = timed(h, OB_K_SERVER, [&] { return ob::launch_server_pass(s, st); });
+  if (e == hipSuccess)
+    e = timed(h, OB_K_SERVER_SCALE, [&] { return ob::launch_server_scales(s, st); });
+  if (e == hipSuccess) e = timed(h, OB_K_UPDATE, [&] { return ob::launch_update(s, lr, st); });
+  if (e != hipSuccess) return fail(h, e);
+  h->steps += 1;
+  h->compressed += 1;
+  return OB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ob_status ob_adam_workspace_bytes(const ob_adam_config* cfg, uint64_t* bytes) {
+  ob_status st = check_config(cfg);
+  if (st != OB_OK) return st;
+  if (bytes == nullptr) return OB_ERR_ARG;
+  *bytes = ob::layout_for(cfg->d, cfg->n_workers).total;
+  return OB_OK;
+}
+
+ob_status ob_adam_init(const ob_adam_config* cfg, void* workspace, uint64_t ws_bytes,
+                       const float* x0, void* stream, ob_adam_t* out) {
+  ob_status st = check_config(cfg);
+  if (st != OB_OK) return st;
+  if (out == nullptr) return OB_ERR_ARG;
+  const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers);
+  if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0 || ws_bytes < l.total)
+    return OB_ERR_WORKSPACE;
+  ob_adam_handle* h = new (std::nothrow) ob_adam_handle();
+  if (h == nullptr) return OB_ERR_ARG;
+  char* base = (char*)workspace;
+  ob::State& s = h->st;
+  s.d = cfg->d;
+  s.n = cfg->n_workers;
+  s.L = cfg->d / cfg->n_workers;
+  s.nseg = (s.L + ob::kSegElems - 1) / ob::kSegElems;
+  s.words = cfg->d / 64;
+  s.grad_bf16 = cfg->grad_dtype == OB_GRAD_BF16;
+  s.beta1 = cfg->beta1;
+  s.beta2 = cfg->beta2;
+  s.eps = cfg->eps;
+  s.x = (float*)(base + l.x);
+  s.m = (float*)(base + l.m);
+  s.v = (float*)(base + l.v);
+  s.u = (float*)(base + l.u);
+  s.c = (float*)(base + l.c);
+  s.wbits = (uint64_t*)(base + l.wbits);
+  s.sbits = (uint64_t*)(base + l.sbits);
+  s.wpart = (double*)(base + l.wpart);
+  s.spart = (double*)(base + l.spart);
+  s.wscale = (float*)(base + l.wscale);
+  s.sscale = (float*)(base + l.sscale);
+  h->stream = (hipStream_t)stream;
+  hipError_t e = hipMemsetAsync(workspace, 0, l.total, h->stream);
+  if (e == hipSuccess && x0 != nullptr)
+    e = hipMemcpyAsync(s.x, x0, sizeof(float) * (size_t)s.d, hipMemcpyDeviceToDevice, h->stream);
+  if (e != hipSuccess) {
+    delete h;
+    return OB_ERR_HIP;
+  }
+  *out = h;
+  return OB_OK;
+}
+
+ob_status ob_adam_warmup_step(ob_adam_t h, const void* const* grads, float lr) {
+  ob_status st = usable(h);
+  if (st != OB_OK) return st;
+  if (h->compressed > 0 || h->staged_open) return OB_ERR_PHASE;
+  ob::GradPtrs g{};
+  st = gather_grads(h, grads, 0, h->st.n, &g);
+  if (st != OB_OK) return st;
+  const int64_t t = h->steps + 1;
+  double p1 = 1.0, p2 = 1.0;
+  for (int64_t i = 0; i < t; ++i) {
+    p1 = p1 * (double)h->st.beta1;
+    p2 = p2 * (double)h->st.beta2;
+  }
+  const float bc1 = (float)(1.0 - p1);
+  const float bc2 = (float)(1.0 - p2);
+  st = fail(h, timed(h, OB_K_WARMUP,
+                     [&] { return ob::launch_warmup(h->st, g, lr, bc1, bc2, h->stream); }));
+  if (st != OB_OK) return st;
+  h->steps = t;
+  h->warm += 1;
+  return OB_OK;
+}
+
+ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float lr) {
+  ob_status st = usable(h);
+  if (st != OB_OK) return st;
+  if (h->warm == 0 || h->staged_open) return OB_ERR_PHASE;
+  ob::GradPtrs g{};
+  st = gather_grads(h, grads, 0, h->st.n, &g);
+  if (st != OB_OK) return st;
+  const bool m_bits = h->compressed > 0;
+  st = fail(h, timed(h, OB_K_WORKER, [&] {
+              return ob::launch_worker_pass(h->st, g, 0, h->st.n, m_bits, h->stream);
+            }));
+  if (st != OB_OK) return st;
+  return finish_step(h, lr);
+}
+
+ob_status ob_adam_compress_worker(ob_adam_t h, int32_t worker, const void* grad) {
+  ob_status st = usable(h);
+  if (st != OB_OK) return st;
+  if (worker < 0 || worker >= h->st.n || grad == nullptr) return OB_ERR_ARG;
+  if (h->warm == 0) return OB_ERR_PHASE;
+  const uint64_t bit = (uint64_t)1 << worker;
+  if (h->staged_open && (h->staged_mask & bit)) return OB_ERR_PHASE;
+  ob::GradPtrs g{};
+  g.p[0] = grad;
+  const bool m_bits = h->compressed > 0;
+  st = fail(h, timed(h, OB_K_WORKER, [&] {
+              return ob::launch_worker_pass(h->st, g, worker, 1, m_bits, h->stream);
+            }));
+  if (st != OB_OK) return st;
+  h->staged_open = true;
+  h->staged_mask |= bit;
+  return OB_OK;
+}
+
+ob_status ob_adam_compressed_finish(ob_adam_t h, float lr) {
+  ob_status st = usable(h);
+  if (st != OB_OK) return st;
+  const uint64_t all = h->st.n == 64 ? ~(uint64_t)0 : (((uint64_t)1 << h->st.n) - 1);
+  if (!h->staged_open || h->staged_mask != all) return OB_ERR_PHASE;
+  st = finish_step(h, lr);
+  if (st != OB_OK) return st;
+  h->staged_open = false;
+  h->staged_mask = 0;
+  return OB_OK;
+}
+
+ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t offset,
+                            int64_t count, void* dst_device) {
+  ob_status st = usable(h);
+  if (st != OB_OK) return st;
+  const ob::State& s = h->st;
+  const bool per_worker =
+      field == OB_E_WORKER || field == OB_BITS_WORKER || field == OB_SCALE_WORKER;
+  if (per_worker && (worker < 0 || worker >= s.n)) return OB_ERR_ARG;
+  int64_t size;
+  switch (field) {
+    case OB_X: case OB_M: case OB_V: case OB_E_WORKER: case OB_E_SERVER: size = s.d; break;
+    case OB_BITS_WORKER: case OB_BITS_SERVER: size = s.words; break;
+    case OB_SCALE_WORKER: case OB_SCALE_SERVER: size = s.n; break;
+    default: return OB_ERR_ARG;
+  }
+  if (offset < 0 || count < 0 || offset > size || count > size - offset) return OB_ERR_ARG;
+  if (count == 0) return OB_OK;
+  if (dst_device == nullptr) return OB_ERR_ARG;
+  hipError_t e = hipSuccess;
+  auto copy = [&](const void* src, size_t elem) {
+    return hipMemcpyAsync(dst_device, (const char*)src + elem * (size_t)offset,
+                          elem * (size_t)count, hipMemcpyDeviceToDevice, h->stream);
+  };
+  const int64_t w = worker;
+  switch (field) {
+    case OB_X: e = copy(s.x, 4); break;
+    case OB_V: e = copy(s.v, 4); break;
+    case OB_M:
+      if (h->compressed > 0)
+        e = ob::launch_decompress_out(s.sbits, s.sscale, s.L, offset, count, (float*)dst_device,
+                                      h->stream);
+      else
+        e = copy(s.m, 4);
+      break;
+    case OB_E_WORKER:
+      e = ob::launch_error_out(s.c + w * s.d, s.wscale + w * s.n, s.L, offset, count,
+                               (float*)dst_device, h->stream);
+      break;
+    case OB_E_SERVER:
+      e = ob::launch_error_out(s.u, s.sscale, s.L, offset, count, (float*)dst_device, h->stream);
+      break;
+    case OB_BITS_WORKER: e = copy(s.wbits + w * s.words, 8); break;
+    case OB_BITS_SERVER: e = copy(s.sbits, 8); break;
+    case OB_SCALE_WORKER: e = copy(s.wscale + w * s.n, 4); break;
+    case OB_SCALE_SERVER: e = copy(s.sscale, 4); break;
+  }
+  return fail(h, e);
+}
+
+ob_status ob_adam_set_state(ob_adam_t h, int32_t field, int64_t offset, int64_t count,
+                            const void* src_device) {
+  ob_status st = usable(h);
+  if (st != OB_OK) return st;
+  const ob::State& s = h->st;
+  float* dst;
+  if (field == OB_X) {
+    dst = s.x;
+  } else if (field == OB_V) {
+    if (h->compressed > 0 || h->staged_open) return OB_ERR_PHASE;
+    dst = s.v;
+  } else {
+    return OB_ERR_ARG;
+  }
+  if (offset < 0 || count < 0 || offset > s.d || count > s.d - offset) return OB_ERR_ARG;
+  if (count == 0) return OB_OK;
+  if (src_device == nullptr) return OB_ERR_ARG;
+  return fail(h, hipMemcpyAsync(dst + offset, src_device, sizeof(float) * (size_t)count,
+                                hipMemcpyDeviceToDevice, h->stream));
+}
+
+ob_status ob_adam_step_count(ob_adam_t h, int64_t* steps, int64_t* compressed_steps) {
+  if (h == nullptr || steps == nullptr || compressed_steps == nullptr) return OB_ERR_ARG;
+  *steps = h->steps;
+  *compressed_steps = h->compressed;
+  return OB_OK;
+}
+
+ob_status ob_adam_set_timing(ob_adam_t h, int32_t max_launches) {
+  if (h == nullptr || max_launches < 0) return OB_ERR_ARG;
+  if (h->poisoned) return OB_ERR_HIP;
+  release_events(h);
+  if (max_launches == 0) return OB_OK;
+  h->ev.assign(2 * (size_t)max_launches, nullptr);
+  for (size_t i = 0; i < h->ev.size(); ++i) {
+    if (hipEventCreate(&h->ev[i]) != hipSuccess) {
+      h->ev.resize(i);
+      release_events(h);
+      return OB_ERR_HIP;
+    }
+  }
+  h->ev_kernel.assign((size_t)max_launches, -1);
+  return OB_OK;
+}
+
+ob_status ob_adam_kernel_times(ob_adam_t h, double* ms, int64_t* launches, int64_t* dropped) {
+  if (h == nullptr || ms == nullptr || launches == nullptr || dropped == nullptr)
+    return OB_ERR_ARG;
+  if (h->poisoned) return OB_ERR_HIP;
+  for (int k = 0; k < OB_NUM_KERNELS; ++k) {
+    ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  *dropped = h->ev_dropped;
+  if (h->ev_used == 0) return OB_OK;
+  if (hipStreamSynchronize(h->stream) != hipSuccess) return fail(h, hipErrorUnknown);
+  for (int64_t i = 0; i < h->ev_used; ++i) {
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, h->ev[2 * i], h->ev[2 * i + 1]) != hipSuccess)
+      return fail(h, hipErrorUnknown);
+    ms[h->ev_kernel[i]] += (double)t;
+    launches[h->ev_kernel[i]] += 1;
+  }
+  return OB_OK;
+}
+
+ob_status ob_adam_destroy(ob_adam_t h) {
+  if (h == nullptr) return OB_ERR_ARG;
+  release_events(h);
+  delete h;
+  return OB_OK;
+}
+
+const char* ob_status_str(ob_status s) {
+  switch (s) {
+    case OB_OK: return "ok";
+    case OB_ERR_ARG: return "invalid argument";
+    case OB_ERR_SHAPE: return "unsupported shape (need d > 0, 1 <= n <= 64, d % (64*n) == 0)";
+    case OB_ERR_PHASE: return "call out of order for the current phase";
+    case OB_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case OB_ERR_HIP: return "HIP runtime error (handle poisoned)";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Launchers of the gfx950 kernels behind the ob_adam C interface.
+// Internal to the library; every launcher enqueues on `stream` and returns
+// hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ob {
+
+constexpr int kMaxWorkersPerLaunch = 64;
+constexpr int kSegElems = 1024;   // elements of one fixed-order segment (one wavefront)
+constexpr int kSegRows = 16;      // rows of 64 elements per segment
+constexpr int64_t kMaxSegsPerChunk = int64_t(1) << 21;
+
+struct GradPtrs {
+  const void* p[kMaxWorkersPerLaunch];
+};
+
+// Device state carved out of the caller's workspace.
+struct State {
+  int64_t d, L, nseg, words;  // words = d/64
+  int n;
+  int grad_bf16;
+  float beta1, beta2, eps;
+  float* x;
+  float* m;
+  float* v;
+  float* u;           // [d]     server: last compensated average (error is derived)
+  float* c;           // [n][d]  worker: last compensated momentum (error is derived)
+  uint64_t* wbits;    // [n][words]
+  uint64_t* sbits;    // [words]
+  double* wpart;      // [n][n][nseg] segment partials of the worker sums of squares
+  double* spart;      // [n][nseg]
+  float* wscale;      // [n][n] row i = worker i, column j = chunk j
+  float* sscale;      // [n]
+};
+
+// Workspace layout: byte offsets of each buffer (256-byte aligned) and total.
+struct Layout {
+  uint64_t x, m, v, u, c, wbits, sbits, wpart, spart, wscale, sscale, total;
+};
+Layout layout_for(int64_t d, int n);
+
+hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1, float bc2,
+                         hipStream_t stream);
+hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw, bool m_bits,
+                              hipStream_t stream);
+hipError_t launch_worker_scales(const State& s, hipStream_t stream);
+hipError_t launch_server_pass(const State& s, hipStream_t stream);
+hipError_t launch_server_scales(const State& s, hipStream_t stream);
+hipError_t launch_update(const State& s, float lr, hipStream_t stream);
+
+// Materialize derived fields for readback.
+hipError_t launch_error_out(const float* comp, const float* scales, int64_t L, int64_t offset,
+                            int64_t count, float* dst, hipStream_t stream);
+hipError_t launch_decompress_out(const uint64_t* bits, const float* scales, int64_t L,
+                                 int64_t offset, int64_t count, float* dst, hipStream_t stream);
+
+}  // namespace ob

@@ -1,0 +1,226 @@
+"""Python binding of libob_adam.so (argument marshalling only).
+
+Functions carry the names of the C interface in include/ob_adam.h and raise
+ObAdamError on a status other than OB_OK.  Every step of the computation runs
+in the library's HIP kernels; PyTorch only provides device memory and the
+stream.  There is no fallback: if the library is missing, importing this
+module fails.
+"""
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library binds to
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libob_adam.so")
+
+OB_OK, OB_ERR_ARG, OB_ERR_SHAPE, OB_ERR_PHASE, OB_ERR_WORKSPACE, OB_ERR_HIP = range(6)
+OB_GRAD_F32, OB_GRAD_BF16 = 0, 1
+(OB_X, OB_M, OB_V, OB_E_WORKER, OB_E_SERVER, OB_BITS_WORKER, OB_BITS_SERVER, OB_SCALE_WORKER,
+ OB_SCALE_SERVER) = range(9)
+
+EXPORTED = ("ob_adam_workspace_bytes", "ob_adam_init", "ob_adam_warmup_step",
+            "ob_adam_compressed_step", "ob_adam_compress_worker", "ob_adam_compressed_finish",
+            "ob_adam_get_state", "ob_adam_set_state", "ob_adam_step_count", "ob_adam_set_timing",
+            "ob_adam_kernel_times", "ob_adam_destroy", "ob_status_str")
+KERNELS = ("warmup", "worker", "worker_scale", "server", "server_scale", "update")
+
+
+class ObAdamError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, ob_status_str(status), status))
+
+
+class ob_adam_config(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int64), ("n_workers", ctypes.c_int32),
+                ("grad_dtype", ctypes.c_int32), ("beta1", ctypes.c_float),
+                ("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libob_adam.so is not built (run __graft_entry__.build()): " + LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, U64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+    cfgp = ctypes.POINTER(ob_adam_config)
+    sig = {
+        "ob_adam_workspace_bytes": [cfgp, ctypes.POINTER(U64)],
+        "ob_adam_init": [cfgp, P, U64, P, P, ctypes.POINTER(P)],
+        "ob_adam_warmup_step": [P, ctypes.POINTER(P), F],
+        "ob_adam_compressed_step": [P, ctypes.POINTER(P), F],
+        "ob_adam_compress_worker": [P, I32, P],
+        "ob_adam_compressed_finish": [P, F],
+        "ob_adam_get_state": [P, I32, I32, I64, I64, P],
+        "ob_adam_set_state": [P, I32, I64, I64, P],
+        "ob_adam_step_count": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
+        "ob_adam_set_timing": [P, I32],
+        "ob_adam_kernel_times": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64),
+                                 ctypes.POINTER(I64)],
+        "ob_adam_destroy": [P],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.ob_status_str.argtypes = [ctypes.c_int]
+    L.ob_status_str.restype = ctypes.c_char_p
+    return L
+
+
+_lib = _load()
+
+
+def _check(status, where):
+    if status != OB_OK:
+        raise ObAdamError(status, where)
+
+
+def ob_status_str(status):
+    return _lib.ob_status_str(status).decode()
+
+
+def make_config(d, n_workers, grad_dtype=OB_GRAD_F32, beta1=0.9, beta2=0.999, eps=1e-8):
+    return ob_adam_config(d, n_workers, grad_dtype, beta1, beta2, eps)
+
+
+def ob_adam_workspace_bytes(cfg):
+    out = ctypes.c_uint64(0)
+    _check(_lib.ob_adam_workspace_bytes(ctypes.byref(cfg), ctypes.byref(out)),
+           "ob_adam_workspace_bytes")
+    return out.value
+
+
+def ob_adam_init(cfg, workspace_ptr, ws_bytes, x0_ptr, stream_ptr):
+    h = ctypes.c_void_p(0)
+    _check(_lib.ob_adam_init(ctypes.byref(cfg), workspace_ptr, ws_bytes, x0_ptr, stream_ptr,
+                             ctypes.byref(h)), "ob_adam_init")
+    return h.value
+
+
+def _ptr_array(ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def ob_adam_warmup_step(h, grad_ptrs, lr):
+    _check(_lib.ob_adam_warmup_step(h, _ptr_array(grad_ptrs), lr), "ob_adam_warmup_step")
+
+
+def ob_adam_compressed_step(h, grad_ptrs, lr):
+    _check(_lib.ob_adam_compressed_step(h, _ptr_array(grad_ptrs), lr), "ob_adam_compressed_step")
+
+
+def ob_adam_compress_worker(h, worker, grad_ptr):
+    _check(_lib.ob_adam_compress_worker(h, worker, grad_ptr), "ob_adam_compress_worker")
+
+
+def ob_adam_compressed_finish(h, lr):
+    _check(_lib.ob_adam_compressed_finish(h, lr), "ob_adam_compressed_finish")
+
+
+def ob_adam_get_state(h, field, worker, offset, count, dst_ptr):
+    _check(_lib.ob_adam_get_state(h, field, worker, offset, count, dst_ptr), "ob_adam_get_state")
+
+
+def ob_adam_set_state(h, field, offset, count, src_ptr):
+    _check(_lib.ob_adam_set_state(h, field, offset, count, src_ptr), "ob_adam_set_state")
+
+
+def ob_adam_step_count(h):
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib.ob_adam_step_count(h, ctypes.byref(a), ctypes.byref(b)), "ob_adam_step_count")
+    return a.value, b.value
+
+
+def ob_adam_set_timing(h, max_launches):
+    _check(_lib.ob_adam_set_timing(h, max_launches), "ob_adam_set_timing")
+
+
+def ob_adam_kernel_times(h):
+    """{kernel name: (milliseconds, launches)} and the dropped-launch count."""
+    ms = (ctypes.c_double * len(KERNELS))()
+    cnt = (ctypes.c_int64 * len(KERNELS))()
+    dropped = ctypes.c_int64(0)
+    _check(_lib.ob_adam_kernel_times(h, ms, cnt, ctypes.byref(dropped)), "ob_adam_kernel_times")
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNELS)}, dropped.value
+
+
+def ob_adam_destroy(h):
+    _check(_lib.ob_adam_destroy(h), "ob_adam_destroy")
+
+
+_FIELD_DTYPE = {OB_X: torch.float32, OB_M: torch.float32, OB_V: torch.float32,
+                OB_E_WORKER: torch.float32, OB_E_SERVER: torch.float32,
+                OB_BITS_WORKER: torch.int64, OB_BITS_SERVER: torch.int64,
+                OB_SCALE_WORKER: torch.float32, OB_SCALE_SERVER: torch.float32}
+
+
+class OneBitAdam:
+    """A handle plus the torch-allocated workspace it lives in."""
+
+    def __init__(self, d, n_workers, grad_dtype=OB_GRAD_F32, beta1=0.9, beta2=0.999, eps=1e-8,
+                 x0=None, device="cuda", stream=None):
+        self.cfg = make_config(d, n_workers, grad_dtype, beta1, beta2, eps)
+        self.d, self.n = d, n_workers
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        self.ws_bytes = ob_adam_workspace_bytes(self.cfg)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        x0p = None
+        if x0 is not None:
+            if x0.dtype != torch.float32 or x0.numel() != d or not x0.is_contiguous():
+                raise ValueError("x0 must be a contiguous float32 tensor of d elements")
+            x0p = x0.data_ptr()
+        self.h = ob_adam_init(self.cfg, self.workspace.data_ptr(), self.ws_bytes, x0p,
+                              self.stream.cuda_stream)
+
+    def _grad_ptrs(self, grads):
+        want = torch.bfloat16 if self.cfg.grad_dtype == OB_GRAD_BF16 else torch.float32
+        ptrs = []
+        for g in grads:
+            if g.dtype != want or g.numel() != self.d or not g.is_contiguous():
+                raise ValueError("gradients must be contiguous %s tensors of d elements" % want)
+            ptrs.append(g.data_ptr())
+        return ptrs
+
+    def warmup_step(self, grads, lr):
+        ob_adam_warmup_step(self.h, self._grad_ptrs(grads), lr)
+
+    def compressed_step(self, grads, lr):
+        ob_adam_compressed_step(self.h, self._grad_ptrs(grads), lr)
+
+    def compress_worker(self, worker, grad):
+        ob_adam_compress_worker(self.h, worker, self._grad_ptrs([grad])[0])
+
+    def compressed_finish(self, lr):
+        ob_adam_compressed_finish(self.h, lr)
+
+    def get(self, field, worker=0, offset=0, count=None):
+        """Device tensor with `count` elements of a field (see include/ob_adam.h)."""
+        size = {OB_BITS_WORKER: self.d // 64, OB_BITS_SERVER: self.d // 64,
+                OB_SCALE_WORKER: self.n, OB_SCALE_SERVER: self.n}.get(field, self.d)
+        if count is None:
+            count = size - offset
+        out = torch.empty(max(count, 0), dtype=_FIELD_DTYPE[field], device=self.device)
+        ob_adam_get_state(self.h, field, worker, offset, count, out.data_ptr() if count else None)
+        return out
+
+    def set(self, field, src, offset=0):
+        if src.dtype != torch.float32 or not src.is_contiguous():
+            raise ValueError("source must be a contiguous float32 tensor")
+        ob_adam_set_state(self.h, field, offset, src.numel(), src.data_ptr())
+
+    @property
+    def steps(self):
+        return ob_adam_step_count(self.h)
+
+    def close(self):
+        if self.h:
+            ob_adam_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

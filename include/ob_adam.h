@@ -1,0 +1,183 @@
+/*
+ * ob_adam: the compression-phase step of 1-bit Adam on one MI355X (gfx950).
+ *
+ * Method: "1-bit Adam: Communication Efficient Large-Scale Training with
+ * Adam's Convergence Speed" (Abstract): full-precision Adam for a warm-up,
+ * then a compression phase in which Adam's variance is a fixed
+ * preconditioner and the momentum is sent with error-compensated 1-bit
+ * compression.  "LIT-278: 1-bit Adam ..." (Key takeaways, Theorem 1
+ * conditions): per-chunk scaling; tag lines SOTA-214 (error feedback on the
+ * momentum) and SOTA-215 (freeze the variance, compress the momentum and
+ * never the update); "What the evidence does not cover" (the compressed
+ * allreduce).
+ *
+ * n data-parallel workers are simulated as n state slabs in one GPU's HBM;
+ * the compressed allreduce is its arithmetic only (worker compress, server
+ * chunk-average and re-compress with server error feedback, decompress).
+ *
+ * Arithmetic contract (the same for every entry point):
+ *  - d parameters, n workers, chunk length L = d/n; chunk j = [j*L, (j+1)*L)
+ *    is server j's share and the unit of every worker's scaling.
+ *  - warm-up step t (1-based): gbar = pairwise-by-levels sum of the n
+ *    gradients (pairs (2i,2i+1), an odd tail passes up) / (float)n;
+ *    m = (b1*m) + ((1-b1)*gbar); v = (b2*v) + ((1-b2)*(gbar*gbar));
+ *    x = x - lr*((m/bc1) / (sqrtf(v/bc2) + eps)), bc = (float)(1 - b^t) with
+ *    b^t formed by t fp64 multiplications.
+ *  - compressed step: per worker i and element, c = ((b1*m) + ((1-b1)*g_i))
+ *    + e_i; per (i, chunk j) scale s_ij = (float)(sqrt(S)/sqrt((double)L)),
+ *    S = fp64 sum of c^2 in the fixed order described below; sign bit =
+ *    (c >= 0); e_i = c - (bit ? s_ij : -s_ij).  Server j: a = pairwise sum
+ *    over workers of (bit ? s_ij : -s_ij) / (float)n; u = a + e_srv; scale
+ *    s_j from u the same way; e_srv = u - (u >= 0 ? s_j : -s_j); m = (u >= 0
+ *    ? s_j : -s_j); x = x - lr*(m / (sqrtf(v) + eps)); v unchanged.
+ *  - fixed fp64 order of a chunk's sum of squares: segments of 1024
+ *    elements; accumulator k of a segment adds the squares of elements
+ *    1024*s + 64*r + k for r = 0..15 in turn; then an xor butterfly over the
+ *    64 accumulators with offsets 32,16,8,4,2,1; then a pairwise sum over the
+ *    segment partials padded with zeros to a power of two.
+ *  - sign words: element k of a d-vector is bit k%64 of uint64 word k/64.
+ *  - no fused multiply-add contraction, no flush of denormals, correctly
+ *    rounded fp32 division and square root.
+ *
+ * Ownership: the caller allocates and owns all device memory (the workspace,
+ * x0, gradients, destinations).  The library allocates no device memory; it
+ * owns only the host handle.  The workspace must stay valid until
+ * ob_adam_destroy.  A handle is not thread-safe.
+ *
+ * Streams: every call is enqueued on the stream given to ob_adam_init (a
+ * hipStream_t passed as void*; NULL = the null stream) and returns without
+ * waiting, except where stated.  Gradients must stay valid until the stream
+ * has passed the call.
+ *
+ * Errors: argument, shape and phase errors return before anything is
+ * enqueued and leave the state untouched.  A HIP launch error returns
+ * OB_ERR_HIP and poisons the handle (later calls return OB_ERR_HIP).
+ * Faults inside kernels surface at the next synchronizing call.  No C++
+ * exception crosses this interface.
+ */
+#ifndef OB_ADAM_H
+#define OB_ADAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ob_adam_handle* ob_adam_t;
+
+typedef enum {
+  OB_OK = 0,
+  OB_ERR_ARG = 1,       /* null pointer, bad dtype, bad worker index, bad range */
+  OB_ERR_SHAPE = 2,     /* d, n do not satisfy the shape rule */
+  OB_ERR_PHASE = 3,     /* call out of order (see each entry point) */
+  OB_ERR_WORKSPACE = 4, /* workspace too small or misaligned */
+  OB_ERR_HIP = 5        /* HIP runtime error; the handle is poisoned */
+} ob_status;
+
+/* Gradient element types. */
+enum { OB_GRAD_F32 = 0, OB_GRAD_BF16 = 1 };
+
+typedef struct {
+  int64_t d;          /* parameters; d > 0 and d % (64*n_workers) == 0 */
+  int32_t n_workers;  /* simulated workers; 1 <= n_workers <= 64 */
+  int32_t grad_dtype; /* OB_GRAD_F32 or OB_GRAD_BF16 (bf16 is widened exactly) */
+  float beta1, beta2, eps;
+} ob_adam_config;
+
+/* Fields for ob_adam_get_state / ob_adam_set_state. */
+enum {
+  OB_X = 0,            /* fp32[d] parameters */
+  OB_M = 1,            /* fp32[d] momentum (after a compressed step: the decompressed server output) */
+  OB_V = 2,            /* fp32[d] variance (frozen in the compression phase) */
+  OB_E_WORKER = 3,     /* fp32[d] error of worker `worker` */
+  OB_E_SERVER = 4,     /* fp32[d] server error */
+  OB_BITS_WORKER = 5,  /* uint64[d/64] last sign words of worker `worker` */
+  OB_BITS_SERVER = 6,  /* uint64[d/64] last server sign words */
+  OB_SCALE_WORKER = 7, /* fp32[n] last scales of worker `worker`, one per chunk */
+  OB_SCALE_SERVER = 8  /* fp32[n] last server scales, one per chunk */
+};
+
+/* Bytes of device workspace a configuration needs (256-byte aligned start). */
+ob_status ob_adam_workspace_bytes(const ob_adam_config* cfg, uint64_t* bytes);
+
+/* Carve the state out of `workspace` (device memory, ws_bytes long, 256-byte
+ * aligned) and set x = x0 (device fp32[d]; NULL = zeros), m = v = errors = 0,
+ * step counter 0.  The copy and the clears are enqueued on `stream`. */
+ob_status ob_adam_init(const ob_adam_config* cfg, void* workspace, uint64_t ws_bytes,
+                       const float* x0, void* stream, ob_adam_t* out);
+
+/* One full-precision Adam step on the average of the n gradients (the
+ * warm-up of the method; "1-bit Adam ..." Abstract; "LIT-278" Key takeaways,
+ * empirical result).  grads: host array of n device pointers, each d
+ * elements of cfg.grad_dtype.  lr: this step's learning rate.
+ * OB_ERR_PHASE after any compressed step. */
+ob_status ob_adam_warmup_step(ob_adam_t h, const void* const* grads, float lr);
+
+/* One compression-phase step (the contract above), all n workers at once.
+ * grads as for ob_adam_warmup_step.  OB_ERR_PHASE before any warm-up step or
+ * while a staged step is open.  The variance is the one left by the last
+ * warm-up step and is never written again. */
+ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float lr);
+
+/* The same step with the gradients supplied one worker at a time, so that a
+ * caller can regenerate each worker's gradient into one buffer (bounded
+ * memory).  Call ob_adam_compress_worker once for every worker w (any order;
+ * `grad` is d device elements and may be reused after the call's work has
+ * passed on the stream), then ob_adam_compressed_finish.  Results are
+ * identical to ob_adam_compressed_step.  OB_ERR_PHASE for a worker given twice
+ * in one step, for finish before all workers, and before any warm-up step. */
+ob_status ob_adam_compress_worker(ob_adam_t h, int32_t worker, const void* grad);
+ob_status ob_adam_compressed_finish(ob_adam_t h, float lr);
+
+/* Copy `count` elements starting at element `offset` of a field (for
+ * OB_E_WORKER, OB_BITS_WORKER and OB_SCALE_WORKER of worker `worker`) into
+ * device memory `dst_device`.  Derived fields (errors, decompressed momentum)
+ * are materialized by a kernel.  Enqueued on the handle's stream; the range
+ * must lie inside the field (OB_ERR_ARG otherwise). */
+ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t offset,
+                            int64_t count, void* dst_device);
+
+/* Overwrite `count` elements of OB_X (always) or OB_V (only before the first
+ * compressed step) from device memory; OB_ERR_ARG for other fields. */
+ob_status ob_adam_set_state(ob_adam_t h, int32_t field, int64_t offset, int64_t count,
+                            const void* src_device);
+
+/* Steps taken so far (warm-up and compressed) and compressed steps taken. */
+ob_status ob_adam_step_count(ob_adam_t h, int64_t* steps, int64_t* compressed_steps);
+
+/* Kernels of a step, for ob_adam_kernel_times. */
+enum {
+  OB_K_WARMUP = 0,        /* warm-up Adam pass */
+  OB_K_WORKER = 1,        /* worker compress pass (all workers of one call) */
+  OB_K_WORKER_SCALE = 2,  /* worker scale finalize */
+  OB_K_SERVER = 3,        /* server average / re-compress pass */
+  OB_K_SERVER_SCALE = 4,  /* server scale finalize */
+  OB_K_UPDATE = 5,        /* decompress + frozen-variance update */
+  OB_NUM_KERNELS = 6
+};
+
+/* Per-kernel timing.  With max_launches > 0, every later kernel launch of a
+ * step is bracketed by a pair of HIP events recorded on the handle's stream,
+ * up to max_launches launches (later ones are counted as dropped); 0 turns
+ * timing off and releases the events.  The events are host-side runtime
+ * objects (no device memory is allocated). */
+ob_status ob_adam_set_timing(ob_adam_t h, int32_t max_launches);
+
+/* Synchronize the stream, then return for each kernel (index OB_K_*) the
+ * summed event-measured duration in milliseconds and the number of timed
+ * launches since timing was enabled, and the number of dropped launches. */
+ob_status ob_adam_kernel_times(ob_adam_t h, double* ms /* [OB_NUM_KERNELS] */,
+                               int64_t* launches /* [OB_NUM_KERNELS] */, int64_t* dropped);
+
+/* Release the host handle (the caller frees the workspace afterwards). */
+ob_status ob_adam_destroy(ob_adam_t h);
+
+/* Static description of a status code. */
+const char* ob_status_str(ob_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,184 @@
+"""Parity of the HIP path (through the C interface) with the CPU oracle.
+
+Sizes are chosen so the oracle finishes in seconds while the kernels see
+several segments, a ragged last segment (chunk length not a multiple of
+1024), chunks shorter than one segment, more segment partials than one
+finalize pass folds, the generic (non power of two) worker count, bf16
+gradients, the first compressed step (fp32 momentum) and later ones
+(momentum kept as server sign words)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import compare_full, gpu_np, host_grads, log, to_device_grad, ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+ob = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global ob
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from communication_compressed_distributed_02_amd import ob_adam
+    ob = ob_adam
+
+
+CASES = [
+    # (name, d, n, bf16, sigma, warm, comp)
+    ("n1_one_segment", 1024, 1, False, 1e-2, 2, 3),
+    ("n3_ragged", 3 * 1472, 3, False, 1e-2, 2, 4),
+    ("n4_ragged", 4 * 3392, 4, False, 1e-2, 2, 4),
+    ("n5_generic", 5 * 2112, 5, False, 1e-2, 1, 3),
+    ("n8_bf16", 8 * 41152, 8, True, 1e-3, 2, 4),
+    ("n16_short_chunks", 16 * 448, 16, False, 1e-3, 2, 3),
+    ("n64_workers", 64 * 1088, 64, False, 1e-3, 2, 3),
+    ("n2_two_fold_groups", 2 * 614976, 2, False, 1e-2, 1, 3),
+    ("n1_eight_fold_groups", 3072064, 1, True, 1e-3, 1, 2),
+]
+
+
+def run_case(d, n, bf16, sigma, warm, comp, staged=False, exact=True, check_every=True):
+    import torch
+    log("case d=%d n=%d bf16=%s warm=%d comp=%d staged=%s" % (d, n, bf16, warm, comp, staged))
+    opt = ob.OneBitAdam(d, n, ob.OB_GRAD_BF16 if bf16 else ob.OB_GRAD_F32)
+    orc = oracle.Oracle(d, n)
+    for t in range(warm + comp):
+        hg = host_grads(d, n, t, sigma=sigma, bf16=bf16)
+        dg = [to_device_grad(g) for g in hg]
+        lr = np.float32(1e-3)
+        if t < warm:
+            opt.warmup_step(dg, lr)
+            orc.warmup_step(hg, lr)
+        elif staged:
+            for w in reversed(range(n)):
+                opt.compress_worker(w, dg[w])
+            opt.compressed_finish(lr)
+            orc.compressed_step(hg, lr)
+        else:
+            opt.compressed_step(dg, lr)
+            orc.compressed_step(hg, lr)
+        torch.cuda.synchronize()
+        if check_every or t == warm + comp - 1:
+            compare_full(opt, orc, t >= warm, exact=exact, where="step %d" % t)
+    return opt, orc
+
+
+@pytest.mark.parametrize("name,d,n,bf16,sigma,warm,comp", CASES, ids=[c[0] for c in CASES])
+def test_parity_small(name, d, n, bf16, sigma, warm, comp):
+    run_case(d, n, bf16, sigma, warm, comp)
+
+
+def test_staged_matches_oracle():
+    run_case(4 * 3392, 4, False, 1e-2, 2, 3, staged=True)
+
+
+def test_device_generator_matches_host():
+    import torch
+    for dist, sigma, bf16 in ((synth.NORMAL, 1e-2, False), (synth.NORMAL, 1e-3, True),
+                              (synth.STUDENT_T3, 1e-3, False)):
+        for elem0, count in ((0, 1 << 16), (123456789, 5000), ((1 << 32) - 100, 300)):
+            t = torch.empty(count, dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+            synth.fill_gpu(t, elem0, 7, 3, dist, sigma)
+            got = t.view(torch.int16).cpu().numpy().view(np.uint16) if bf16 else t.cpu().numpy()
+            want = synth.fill_cpu(count, elem0, 7, 3, dist, sigma, bf16)
+            np.testing.assert_array_equal(got.view(np.uint16 if bf16 else np.uint32),
+                                          want.view(np.uint16 if bf16 else np.uint32))
+
+
+def test_c1_full_parity_every_step():
+    """The small workload (d = 2^20, n = 4, 3 warm-up + 7 compressed steps,
+    fp32 N(0, 1e-2) gradients from the device generator), every field at
+    every step; fp32 state is also bit-identical."""
+    import torch
+    from synth import workloads as W
+    w = W.make("c1")
+    opt = ob.OneBitAdam(w.d, w.n, ob.OB_GRAD_F32, w.beta1, w.beta2, w.eps)
+    orc = oracle.Oracle(w.d, w.n, w.beta1, w.beta2, w.eps)
+    g = torch.empty((w.n, w.d), dtype=torch.float32, device="cuda")
+    for t in range(w.steps):
+        for i in range(w.n):
+            synth.fill_gpu(g[i], 0, t, i, w.dist, w.sigma)
+        hg = [W.cpu_grad(w, i, t, 0, w.d) for i in range(w.n)]
+        lr = w.lr_at(t)
+        if t < w.warmup:
+            opt.warmup_step(list(g), lr)
+            orc.warmup_step(hg, lr)
+        else:
+            opt.compressed_step(list(g), lr)
+            orc.compressed_step(hg, lr)
+        torch.cuda.synchronize()
+        compare_full(opt, orc, t >= w.warmup, exact=True, where="c1 step %d" % t)
+    assert opt.steps == (10, 7)
+
+
+def test_run_twice_is_bitwise_identical():
+    a, _ = run_case(8 * 41152, 8, True, 1e-3, 2, 3, check_every=False)
+    b, _ = run_case(8 * 41152, 8, True, 1e-3, 2, 3, check_every=False)
+    for f in (ob.OB_X, ob.OB_E_SERVER, ob.OB_BITS_SERVER):
+        np.testing.assert_array_equal(gpu_np(a, f), gpu_np(b, f))
+    for wk in range(8):
+        np.testing.assert_array_equal(gpu_np(a, ob.OB_E_WORKER, wk), gpu_np(b, ob.OB_E_WORKER, wk))
+
+
+def test_phase_rules_and_ranges():
+    import torch
+    d, n = 4096, 4
+    opt = ob.OneBitAdam(d, n)
+    g = [torch.zeros(d, device="cuda") for _ in range(n)]
+    with pytest.raises(ob.ObAdamError) as e:
+        opt.compressed_step(g, 1e-3)
+    assert e.value.status == ob.OB_ERR_PHASE
+    with pytest.raises(ob.ObAdamError) as e:
+        opt.compress_worker(0, g[0])
+    assert e.value.status == ob.OB_ERR_PHASE
+    opt.warmup_step(g, 1e-3)
+    opt.compress_worker(2, g[2])
+    with pytest.raises(ob.ObAdamError) as e:
+        opt.compress_worker(2, g[2])
+    assert e.value.status == ob.OB_ERR_PHASE
+    with pytest.raises(ob.ObAdamError) as e:
+        opt.compressed_finish(1e-3)
+    assert e.value.status == ob.OB_ERR_PHASE
+    with pytest.raises(ob.ObAdamError) as e:
+        opt.compressed_step(g, 1e-3)
+    assert e.value.status == ob.OB_ERR_PHASE
+    for w in (0, 1, 3):
+        opt.compress_worker(w, g[w])
+    opt.compressed_finish(1e-3)
+    assert opt.steps == (2, 1)
+    with pytest.raises(ob.ObAdamError) as e:
+        opt.warmup_step(g, 1e-3)
+    assert e.value.status == ob.OB_ERR_PHASE
+    with pytest.raises(ob.ObAdamError) as e:
+        opt.set(ob.OB_V, torch.zeros(4, device="cuda"))
+    assert e.value.status == ob.OB_ERR_PHASE
+    with pytest.raises(ob.ObAdamError) as e:
+        opt.get(ob.OB_X, 0, d - 2, 4)
+    assert e.value.status == ob.OB_ERR_ARG
+    with pytest.raises(ob.ObAdamError) as e:
+        opt.get(ob.OB_E_WORKER, n, 0, 4)
+    assert e.value.status == ob.OB_ERR_ARG
+    with pytest.raises(ob.ObAdamError) as e:
+        opt.compress_worker(n, g[0])
+    assert e.value.status == ob.OB_ERR_ARG
+    # errors leave the state untouched: the step still runs and counts
+    opt.compressed_step(g, 1e-3)
+    assert opt.steps == (3, 2)
+    # zero gradients and zero momentum: scales 0, all sign bits set
+    assert np.all(gpu_np(opt, ob.OB_BITS_SERVER) == np.uint64(0xFFFFFFFFFFFFFFFF))
+    assert np.all(gpu_np(opt, ob.OB_SCALE_SERVER) == 0)
+
+
+def test_slices_match_whole_fields():
+    opt, orc = run_case(4 * 3392, 4, False, 1e-2, 1, 2, check_every=False)
+    for f, of in ((ob.OB_E_WORKER, oracle.E_WORKER), (ob.OB_M, oracle.M)):
+        whole = orc.get(of, 1)
+        part = gpu_np(opt, f, 1, 1000, 3000)
+        assert ulp_diff(part, whole[1000:4000]) == 0
+    bits = gpu_np(opt, ob.OB_BITS_WORKER, 2, 5, 7)
+    np.testing.assert_array_equal(bits, orc.get(oracle.BITS_WORKER, 2)[5:12])
