@@ -100,6 +100,20 @@ def cpu_baseline(w, steps=1):
             "s_per_step_extrapolated": per_step}
 
 
+def copy_calibration(mib):
+    """A plain copy of known size: each dispatch reads and writes mib MiB."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                      "dispatches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,7 +122,13 @@ def main():
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=1)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch's device copy of MIB MiB five times (a kernel of "
+                         "known traffic for scaling profiler byte counters) and exit")
     a = ap.parse_args()
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return
     if a.gpus != 1:
         print("bench.py measures one GPU only: the simulated workers live on one MI355X; "
               "--gpus %d is not supported" % a.gpus, file=sys.stderr)

@@ -153,6 +153,7 @@ ob_status ob_adam_init(const ob_adam_config* cfg, void* workspace, uint64_t ws_b
   s.sbits = (uint64_t*)(base + l.sbits);
   s.wpart = (double*)(base + l.wpart);
   s.spart = (double*)(base + l.spart);
+  s.fold = (double*)(base + l.fold);
   s.wscale = (float*)(base + l.wscale);
   s.sscale = (float*)(base + l.sscale);
   h->stream = (hipStream_t)stream;

@@ -32,13 +32,14 @@ struct State {
   uint64_t* sbits;    // [words]
   double* wpart;      // [n][n][nseg] segment partials of the worker sums of squares
   double* spart;      // [n][nseg]
+  double* fold;       // [n][n][groups] group results of the scale finalize
   float* wscale;      // [n][n] row i = worker i, column j = chunk j
   float* sscale;      // [n]
 };
 
 // Workspace layout: byte offsets of each buffer (256-byte aligned) and total.
 struct Layout {
-  uint64_t x, m, v, u, c, wbits, sbits, wpart, spart, wscale, sscale, total;
+  uint64_t x, m, v, u, c, wbits, sbits, wpart, spart, fold, wscale, sscale, total;
 };
 Layout layout_for(int64_t d, int n);
 

@@ -35,17 +35,46 @@
 namespace ob {
 namespace {
 
-constexpr int kBlock = 256;
+#ifndef OB_BLOCK
+#define OB_BLOCK 256
+#endif
+constexpr int kBlock = OB_BLOCK;
 constexpr int kWavesPerBlock = kBlock / 64;
+
+// Launch-shape knobs (blocks along a chunk's segments per grid row).
+#ifndef OB_WORKER_BLOCKS_PER_ROW
+#define OB_WORKER_BLOCKS_PER_ROW (1 << 20)
+#endif
+#ifndef OB_SERVER_BLOCKS_PER_ROW
+#define OB_SERVER_BLOCKS_PER_ROW (1 << 20)
+#endif
+#ifndef OB_UPDATE_BLOCKS
+#define OB_UPDATE_BLOCKS (1 << 20)
+#endif
+
+// Streamed (read-once / write-once per step) accesses are non-temporal: the
+// step's working set is many times the caches, so nothing streamed is reused
+// before eviction.
+#ifndef OB_NO_NT_STREAM
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, T v) { __builtin_nontemporal_store(v, p); }
+#else
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) { return *p; }
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, T v) { *p = v; }
+#endif
 
 // Index of this wavefront in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_in_block() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
-__device__ __forceinline__ float grad_value(const float* g, int64_t k) { return g[k]; }
+__device__ __forceinline__ float grad_value(const float* g, int64_t k) { return ld_stream(g + k); }
 __device__ __forceinline__ float grad_value(const uint16_t* g, int64_t k) {
-  return __uint_as_float((uint32_t)g[k] << 16);  // bf16 -> fp32, exact
+  return __uint_as_float((uint32_t)ld_stream(g + k) << 16);  // bf16 -> fp32, exact
 }
 
 // +s where bit `lane` of the uniform word is set, -s elsewhere.
@@ -134,14 +163,66 @@ __device__ __forceinline__ void worker_row(const GT* __restrict__ g, float* __re
                                            int64_t k, float sp, float beta1, float ob1,
                                            double& acc, uint64_t& word) {
   const float gv = grad_value(g, k);
-  const float cp = c[k];
+  const float cp = ld_stream(c + k);
   const float e = cp - (cp >= 0.0f ? sp : -sp);
   const float mv = MBITS ? signed_scale(mword, ms) : m[k];
   const float cv = ((beta1 * mv) + (ob1 * gv)) + e;
-  c[k] = cv;
+  st_stream(c + k, cv);
   word = __ballot(cv >= 0.0f);
   acc = add_square(acc, cv);
 }
+
+// One full segment: all 32 loads are issued before any use.
+template <typename GT, bool MBITS>
+struct SegIn {
+  float g[kSegRows];
+  float c[kSegRows];
+  float m[kSegRows];
+};
+
+template <typename GT, bool MBITS>
+__device__ __forceinline__ void load_segment(SegIn<GT, MBITS>& in, const GT* __restrict__ g,
+                                             const float* __restrict__ c,
+                                             const float* __restrict__ m,
+                                             const uint64_t* __restrict__ sbits, float ms,
+                                             int64_t base, int lane) {
+#pragma unroll
+  for (int r = 0; r < kSegRows; ++r) {
+    in.g[r] = grad_value(g, base + 64 * r + lane);
+    in.c[r] = ld_stream(c + base + 64 * r + lane);
+  }
+#pragma unroll
+  for (int r = 0; r < kSegRows; ++r)
+    in.m[r] = MBITS ? signed_scale(sbits[(base >> 6) + r], ms) : m[base + 64 * r + lane];
+}
+
+template <typename GT, bool MBITS>
+__device__ __forceinline__ void compute_segment(const SegIn<GT, MBITS>& in, float* __restrict__ c,
+                                                uint64_t* __restrict__ bits,
+                                                double* __restrict__ part, int64_t base,
+                                                int lane, float sp, float beta1, float ob1) {
+  double acc = 0.0;
+  uint64_t mine = 0;
+#pragma unroll
+  for (int r = 0; r < kSegRows; ++r) {
+    const float e = in.c[r] - (in.c[r] >= 0.0f ? sp : -sp);
+    const float cv = ((beta1 * in.m[r]) + (ob1 * in.g[r])) + e;
+    st_stream(c + base + 64 * r + lane, cv);
+    const uint64_t word = __ballot(cv >= 0.0f);
+    mine = lane == r ? word : mine;
+    acc = add_square(acc, cv);
+  }
+  acc = butterfly(acc);
+  if (lane < kSegRows) bits[(base >> 6) + lane] = mine;
+  if (lane == 0) *part = acc;
+}
+
+#ifndef OB_WORKER_SEGS_PER_WAVE
+#define OB_WORKER_SEGS_PER_WAVE 1
+#endif
+#ifndef OB_WORKER_ROWWISE
+#define OB_WORKER_ROWWISE 1
+#endif
 
 template <typename GT, bool MBITS>
 __global__ void __launch_bounds__(kBlock)
@@ -150,6 +231,7 @@ __global__ void __launch_bounds__(kBlock)
                   const float* __restrict__ sscale, float* __restrict__ cbuf,
                   const float* __restrict__ wscale, uint64_t* __restrict__ wbits,
                   double* __restrict__ wpart, float beta1, float ob1) {
+  constexpr int SPW = OB_WORKER_SEGS_PER_WAVE;
   const int lane = threadIdx.x & 63;
   const int wi = (int)blockIdx.y / n;  // worker within this launch
   const int j = (int)blockIdx.y - wi * n;
@@ -157,28 +239,57 @@ __global__ void __launch_bounds__(kBlock)
   const GT* __restrict__ gp = (const GT*)g.p[wi];
   float* __restrict__ c = cbuf + (int64_t)w * d;
   uint64_t* __restrict__ bits = wbits + (int64_t)w * words;
+  double* __restrict__ part = wpart + ((int64_t)w * n + j) * nseg;
   const float sp = wscale[w * n + j];  // this worker's scale of chunk j, previous step
   const float ms = MBITS ? sscale[j] : 0.0f;
+  const int64_t full = L / kSegElems;  // segments with all 16 rows
   const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); s < nseg;
-       s += nwave) {
-    const int64_t q0 = s * kSegElems;
-    const int64_t left = (L - q0) >> 6;
-    const int rows = left < kSegRows ? (int)left : kSegRows;
-    const int64_t base = (int64_t)j * L + q0;  // global index of the segment's first element
-    const int64_t wbase = base >> 6;
-    double acc = 0.0;
-    uint64_t mine = 0;
-    if (rows == kSegRows) {
+  for (int64_t s0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave_in_block()) * SPW; s0 < nseg;
+       s0 += nwave * SPW) {
+#if OB_WORKER_ROWWISE
+    if (s0 + SPW <= full) {
 #pragma unroll
-      for (int r = 0; r < kSegRows; ++r) {
-        uint64_t word;
-        const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
-        worker_row<GT, MBITS>(gp, c, m, mword, ms, base + 64 * r + lane, sp, beta1, ob1, acc,
-                              word);
-        mine = lane == r ? word : mine;
+      for (int q = 0; q < SPW; ++q) {
+        const int64_t base = (int64_t)j * L + (s0 + q) * kSegElems;
+        const int64_t wbase = base >> 6;
+        double acc = 0.0;
+        uint64_t mine = 0;
+#pragma unroll
+        for (int r = 0; r < kSegRows; ++r) {
+          uint64_t word;
+          const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
+          worker_row<GT, MBITS>(gp, c, m, mword, ms, base + 64 * r + lane, sp, beta1, ob1, acc,
+                                word);
+          mine = lane == r ? word : mine;
+        }
+        acc = butterfly(acc);
+        if (lane < kSegRows) bits[wbase + lane] = mine;
+        if (lane == 0) part[s0 + q] = acc;
       }
-    } else {
+      continue;
+    }
+#else
+    if (s0 + SPW <= full) {
+      SegIn<GT, MBITS> in[SPW];
+#pragma unroll
+      for (int q = 0; q < SPW; ++q)
+        load_segment<GT, MBITS>(in[q], gp, c, m, sbits, ms, (int64_t)j * L + (s0 + q) * kSegElems,
+                                lane);
+#pragma unroll
+      for (int q = 0; q < SPW; ++q)
+        compute_segment<GT, MBITS>(in[q], c, bits, part + s0 + q,
+                                   (int64_t)j * L + (s0 + q) * kSegElems, lane, sp, beta1, ob1);
+      continue;
+    }
+#endif
+    for (int64_t s = s0; s < s0 + SPW && s < nseg; ++s) {
+      const int64_t q0 = s * kSegElems;
+      const int64_t left = (L - q0) >> 6;
+      const int rows = left < kSegRows ? (int)left : kSegRows;
+      const int64_t base = (int64_t)j * L + q0;  // global index of the segment's first element
+      const int64_t wbase = base >> 6;
+      double acc = 0.0;
+      uint64_t mine = 0;
       for (int r = 0; r < rows; ++r) {
         uint64_t word;
         const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
@@ -186,64 +297,79 @@ __global__ void __launch_bounds__(kBlock)
                               word);
         mine = lane == r ? word : mine;
       }
+      acc = butterfly(acc);
+      if (lane < rows) bits[wbase + lane] = mine;
+      if (lane == 0) part[s] = acc;
     }
-    acc = butterfly(acc);
-    if (lane < rows) bits[wbase + lane] = mine;
-    if (lane == 0) wpart[((int64_t)w * n + j) * nseg + s] = acc;
   }
 }
 
 // ---------------------------------------------------------- scale finalize --
-// One block per (worker, chunk) or per chunk: pairwise sum of the segment
-// partials (padded with zeros to a power of two), then
-// scale = (float)(sqrt(S) / sqrt((double)L)).
-constexpr int kGroup = 2 * kBlock;  // partials folded per pass of the block
-constexpr int kMaxGroups = 4096;
+// The pairwise sum over a row's segment partials (padded with zeros to a
+// power of two, width W) is split at aligned subtrees of kGroup = 512
+// partials: phase 1 folds every group in parallel (grid = groups x rows),
+// phase 2 folds a row's group results (a power of two of them) and forms
+// scale = (float)(sqrt(S) / sqrt((double)L)).  Zero padding contributes +0
+// to every sum it enters, so padding a short row up to one whole group gives
+// the same value as its own power-of-two width.
+constexpr int kGroup = 2 * kBlock;
+
+// Group results per row over all fold levels of a row of nseg partials.
+int64_t fold_doubles_per_row(int64_t nseg) {
+  int64_t total = 0;
+  for (int64_t cnt = nseg;;) {
+    int64_t width = 1;
+    while (width < cnt) width <<= 1;
+    if (width <= kGroup) return total;
+    cnt = width / kGroup;
+    total += cnt;
+  }
+}
+
+// Pairwise fold of the 2*kBlock values a[t], b[t] (t = thread) held as pairs
+// (a[t] = element 2t, b[t] = element 2t+1); returns the sum in thread 0.
+__device__ double block_pairwise(double a, double b, double* red) {
+  const int t = threadIdx.x;
+  red[t] = a + b;
+  __syncthreads();
+  for (int h = kBlock / 2; h >= 1; h >>= 1) {
+    double val = 0.0;
+    if (t < h) val = red[2 * t] + red[2 * t + 1];
+    __syncthreads();
+    if (t < h) red[t] = val;
+    __syncthreads();
+  }
+  return red[0];
+}
 
 __global__ void __launch_bounds__(kBlock)
-    scale_kernel(const double* __restrict__ part, int64_t nseg, int64_t L, int rows_per_launch,
-                 int part_row0, float* __restrict__ scale_out) {
+    fold_groups_kernel(const double* __restrict__ part, int64_t nseg, int64_t ngroups,
+                       double* __restrict__ out) {
   __shared__ double red[kBlock];
-  __shared__ double grpA[kMaxGroups];
-  __shared__ double grpB[kMaxGroups / 2];
   const int t = threadIdx.x;
-  const int row = blockIdx.x;
-  const double* __restrict__ p = part + (int64_t)(part_row0 + row) * nseg;
-  int64_t width = 1;
-  while (width < nseg) width <<= 1;
-  const int64_t ngroups = width <= kGroup ? 1 : width / kGroup;
-  for (int64_t gi = 0; gi < ngroups; ++gi) {
-    const int64_t i0 = gi * kGroup + 2 * t;
-    const double a = i0 < nseg ? p[i0] : 0.0;
-    const double b = i0 + 1 < nseg ? p[i0 + 1] : 0.0;
-    red[t] = a + b;
-    __syncthreads();
-    for (int h = kBlock / 2; h >= 1; h >>= 1) {
-      double val = 0.0;
-      if (t < h) val = red[2 * t] + red[2 * t + 1];
-      __syncthreads();
-      if (t < h) red[t] = val;
-      __syncthreads();
-    }
-    if (t == 0) grpA[gi] = red[0];
-    __syncthreads();
-  }
-  // pairwise over the group results (a power of two of them)
-  double* src = grpA;
-  double* dst = grpB;
-  for (int64_t cnt = ngroups; cnt > 1; cnt >>= 1) {
-    const int64_t half = cnt >> 1;
-    for (int64_t i = t; i < half; i += kBlock) dst[i] = src[2 * i] + src[2 * i + 1];
-    __syncthreads();
-    double* tmp = src;
-    src = dst;
-    dst = tmp;
-  }
-  (void)rows_per_launch;
-  if (t == 0) {
-    const double S = src[0];
-    scale_out[row] = (float)(sqrt(S) / sqrt((double)L));
-  }
+  const int64_t g = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const double* __restrict__ p = part + row * nseg;
+  const int64_t i0 = g * kGroup + 2 * t;
+  const double a = i0 < nseg ? p[i0] : 0.0;
+  const double b = i0 + 1 < nseg ? p[i0 + 1] : 0.0;
+  const double sum = block_pairwise(a, b, red);
+  if (t == 0) out[row * ngroups + g] = sum;
+}
+
+__global__ void __launch_bounds__(kBlock)
+    scale_kernel(const double* __restrict__ vals, int64_t count, int64_t L,
+                 float* __restrict__ scale_out) {
+  // count <= kGroup values per row, zero padded to kGroup
+  __shared__ double red[kBlock];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const double* __restrict__ p = vals + row * count;
+  const int64_t i0 = 2 * t;
+  const double a = i0 < count ? p[i0] : 0.0;
+  const double b = i0 + 1 < count ? p[i0 + 1] : 0.0;
+  const double S = block_pairwise(a, b, red);
+  if (t == 0) scale_out[row] = (float)(sqrt(S) / sqrt((double)L));
 }
 
 // ------------------------------------------------------------- server pass --
@@ -262,6 +388,36 @@ __device__ __forceinline__ float worker_average(const uint64_t* __restrict__ wbi
     for (int w = 0; w < n; ++w) vals[w] = signed_scale(wbits[(int64_t)w * words + row], ws[w]);
     return pairwise_sum_any(vals, n) / (float)n;
   }
+}
+
+// Full segment, NW a power of two: the 16 sign words of one worker are one
+// uniform 128-byte burst; workers are folded into per-row stacks in worker
+// order so that the result is exactly the pairwise-by-levels sum (merging
+// level l whenever bit l of the worker index is set, left operand first).
+template <int NW>
+__device__ __forceinline__ void server_average_segment(const uint64_t* __restrict__ wbits,
+                                                       int64_t words, int64_t wbase,
+                                                       const float* ws, float* avg) {
+  constexpr int LEVELS = NW == 1 ? 1 : (NW == 2 ? 2 : NW == 4 ? 3 : NW == 8 ? 4 : NW == 16 ? 5
+                                        : NW == 32 ? 6 : 7);
+  float stack[LEVELS][kSegRows];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint64_t* __restrict__ wp = wbits + (int64_t)w * words + wbase;
+    float v[kSegRows];
+#pragma unroll
+    for (int r = 0; r < kSegRows; ++r) v[r] = signed_scale(wp[r], ws[w]);
+    int lvl = 0;
+#pragma unroll
+    for (int x = w; x & 1; x >>= 1, ++lvl) {
+#pragma unroll
+      for (int r = 0; r < kSegRows; ++r) v[r] = stack[lvl][r] + v[r];
+    }
+#pragma unroll
+    for (int r = 0; r < kSegRows; ++r) stack[lvl][r] = v[r];
+  }
+#pragma unroll
+  for (int r = 0; r < kSegRows; ++r) avg[r] = stack[LEVELS - 1][r] / (float)NW;
 }
 
 template <int NW>
@@ -288,6 +444,28 @@ __global__ void __launch_bounds__(kBlock)
     const int64_t wbase = base >> 6;
     double acc = 0.0;
     uint64_t mine = 0;
+    if constexpr (NW > 0) {
+      if (rows == kSegRows) {
+        float up[kSegRows];
+#pragma unroll
+        for (int r = 0; r < kSegRows; ++r) up[r] = ld_stream(u + base + 64 * r + lane);
+        float avg[kSegRows];
+        server_average_segment<NW>(wbits, words, wbase, ws, avg);
+#pragma unroll
+        for (int r = 0; r < kSegRows; ++r) {
+          const float e = up[r] - (up[r] >= 0.0f ? sp : -sp);
+          const float uv = avg[r] + e;
+          st_stream(u + base + 64 * r + lane, uv);
+          const uint64_t word = __ballot(uv >= 0.0f);
+          mine = lane == r ? word : mine;
+          acc = add_square(acc, uv);
+        }
+        acc = butterfly(acc);
+        if (lane < kSegRows) sbits[wbase + lane] = mine;
+        if (lane == 0) spart[(int64_t)j * nseg + s] = acc;
+        continue;
+      }
+    }
     for (int r = 0; r < rows; ++r) {
       const int64_t k = base + 64 * r + lane;
       const float up = u[k];
@@ -308,6 +486,10 @@ __global__ void __launch_bounds__(kBlock)
 // ------------------------------------------------------------------ update --
 // m = (bit ? s_j : -s_j); x = x - lr * (m / (sqrtf(v) + eps)).  A wave owns 16
 // consecutive rows of the flat vector; the chunk of a row is row*64 / L.
+__device__ __forceinline__ float update_one(float x, float v, float mv, float lr, float eps) {
+  return x - lr * (mv / (sqrtf(v) + eps));
+}
+
 __global__ void __launch_bounds__(kBlock)
     update_kernel(int64_t words, int64_t L, const uint64_t* __restrict__ sbits,
                   const float* __restrict__ sscale, const float* __restrict__ v,
@@ -320,12 +502,28 @@ __global__ void __launch_bounds__(kBlock)
        gi += nwave) {
     const int64_t r0 = gi * kSegRows;
     const int rows = words - r0 < kSegRows ? (int)(words - r0) : kSegRows;
-    for (int r = 0; r < rows; ++r) {
-      const int64_t row = r0 + r;
-      const float s = sscale[row / rows_per_chunk];
-      const int64_t k = row * 64 + lane;
-      const float mv = signed_scale(sbits[row], s);
-      x[k] = x[k] - lr * (mv / (sqrtf(v[k]) + eps));
+    const int64_t j0 = r0 / rows_per_chunk;
+    // the 16 rows lie in one chunk unless a chunk boundary falls inside them
+    const bool one_chunk = rows == kSegRows && (r0 + kSegRows - 1) / rows_per_chunk == j0;
+    if (one_chunk) {
+      const float s = sscale[j0];
+      float xv[kSegRows], vv[kSegRows];
+#pragma unroll
+      for (int r = 0; r < kSegRows; ++r) {
+        xv[r] = ld_stream(x + (r0 + r) * 64 + lane);
+        vv[r] = ld_stream(v + (r0 + r) * 64 + lane);
+      }
+#pragma unroll
+      for (int r = 0; r < kSegRows; ++r)
+        st_stream(x + (r0 + r) * 64 + lane,
+                  update_one(xv[r], vv[r], signed_scale(sbits[r0 + r], s), lr, eps));
+    } else {
+      for (int r = 0; r < rows; ++r) {
+        const int64_t row = r0 + r;
+        const float s = sscale[row / rows_per_chunk];
+        const int64_t k = row * 64 + lane;
+        x[k] = update_one(x[k], v[k], signed_scale(sbits[row], s), lr, eps);
+      }
     }
   }
 }
@@ -384,6 +582,7 @@ Layout layout_for(int64_t d, int n) {
   l.sbits = take(8 * (ud / 64));
   l.wpart = take(8 * un * un * nseg);
   l.spart = take(8 * un * nseg);
+  l.fold = take(8 * un * un * (uint64_t)fold_doubles_per_row((int64_t)nseg));
   l.wscale = take(4 * un * un);
   l.sscale = take(4 * un);
   l.total = off;
@@ -421,7 +620,8 @@ hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1,
 hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw, bool m_bits,
                               hipStream_t stream) {
   const float ob1 = 1.0f - s.beta1;
-  dim3 grid(grid_for(s.nseg, kWavesPerBlock, 1 << 20), (unsigned)(nw * s.n));
+  dim3 grid(grid_for(s.nseg, kWavesPerBlock * OB_WORKER_SEGS_PER_WAVE, OB_WORKER_BLOCKS_PER_ROW),
+            (unsigned)(nw * s.n));
 #define OB_WORK(GT, MB)                                                                          \
   worker_kernel<GT, MB><<<grid, kBlock, 0, stream>>>(g, w0, s.d, s.L, s.n, s.nseg, s.words, s.m, \
                                                      s.sbits, s.sscale, s.c, s.wscale, s.wbits,  \
@@ -435,13 +635,38 @@ hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw,
   return hipGetLastError();
 }
 
-hipError_t launch_worker_scales(const State& s, hipStream_t stream) {
-  scale_kernel<<<s.n * s.n, kBlock, 0, stream>>>(s.wpart, s.nseg, s.L, s.n * s.n, 0, s.wscale);
+// Scales of `rows` rows of segment partials (nseg per row) into scale_out:
+// fold aligned groups of kGroup until at most kGroup values remain per row,
+// then the last fold and the scale.  `fold` holds rows *
+// fold_doubles_per_row(nseg) doubles.
+static hipError_t launch_scales(const double* part, int64_t nseg, int64_t L, int rows,
+                                double* fold, float* scale_out, hipStream_t stream) {
+  const double* cur = part;
+  int64_t cnt = nseg;
+  double* out = fold;
+  for (;;) {
+    int64_t width = 1;
+    while (width < cnt) width <<= 1;
+    if (width <= kGroup) break;
+    const int64_t ngroups = width / kGroup;
+    fold_groups_kernel<<<dim3((unsigned)ngroups, (unsigned)rows), kBlock, 0, stream>>>(
+        cur, cnt, ngroups, out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    cur = out;
+    cnt = ngroups;
+    out += (int64_t)rows * ngroups;
+  }
+  scale_kernel<<<rows, kBlock, 0, stream>>>(cur, cnt, L, scale_out);
   return hipGetLastError();
 }
 
+hipError_t launch_worker_scales(const State& s, hipStream_t stream) {
+  return launch_scales(s.wpart, s.nseg, s.L, s.n * s.n, s.fold, s.wscale, stream);
+}
+
 hipError_t launch_server_pass(const State& s, hipStream_t stream) {
-  dim3 grid(grid_for(s.nseg, kWavesPerBlock, 1 << 20), (unsigned)s.n);
+  dim3 grid(grid_for(s.nseg, kWavesPerBlock, OB_SERVER_BLOCKS_PER_ROW), (unsigned)s.n);
 #define OB_SRV(NW)                                                                        \
   server_kernel<NW><<<grid, kBlock, 0, stream>>>(s.L, s.n, s.nseg, s.words, s.wbits,      \
                                                  s.wscale, s.u, s.sscale, s.sbits, s.spart)
@@ -460,13 +685,12 @@ hipError_t launch_server_pass(const State& s, hipStream_t stream) {
 }
 
 hipError_t launch_server_scales(const State& s, hipStream_t stream) {
-  scale_kernel<<<s.n, kBlock, 0, stream>>>(s.spart, s.nseg, s.L, s.n, 0, s.sscale);
-  return hipGetLastError();
+  return launch_scales(s.spart, s.nseg, s.L, s.n, s.fold, s.sscale, stream);
 }
 
 hipError_t launch_update(const State& s, float lr, hipStream_t stream) {
   const int64_t groups = (s.words + kSegRows - 1) / kSegRows;
-  update_kernel<<<grid_for(groups, kWavesPerBlock, 1 << 20), kBlock, 0, stream>>>(
+  update_kernel<<<grid_for(groups, kWavesPerBlock, OB_UPDATE_BLOCKS), kBlock, 0, stream>>>(
       s.words, s.L, s.sbits, s.sscale, s.v, s.x, lr, s.eps);
   return hipGetLastError();
 }

@@ -38,10 +38,10 @@ class ob_adam_config(ctypes.Structure):
                 ("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError("libob_adam.so is not built (run __graft_entry__.build()): " + LIB_PATH)
-    L = ctypes.CDLL(LIB_PATH)
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError("libob_adam.so is not built (run __graft_entry__.build()): " + path)
+    L = ctypes.CDLL(path)
     P, I32, I64, U64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
     cfgp = ctypes.POINTER(ob_adam_config)
     sig = {
