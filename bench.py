@@ -27,7 +27,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "compressed-step params·workers/sec and achieved HBM GB/s (% of peak), 1 GPU"
 KERNEL_SRC = os.path.join(ROOT, "communication_compressed_distributed_02_amd", "csrc",
                           "ob_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_worker_pass_c2.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "worker_pass_c2_counters.txt")
 
 
 def alg_bytes(w):
@@ -65,13 +65,18 @@ def kernel_sha():
 def load_traffic(workload):
     """Counter-measured HBM bytes per worker-pass launch, if they were taken
     on the current kernel source (else None)."""
+    t = None
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        for line in open(TRAFFIC_FILE):
+            if line.startswith("traffic_record: "):
+                t = json.loads(line[len("traffic_record: "):])
     except (OSError, ValueError):
+        return None
+    if t is None:
         return None
     if t.get("kernel_source_sha") != kernel_sha() or t.get("workload") != workload:
         return None
-    return t.get("bytes_per_launch")
+    return t
 
 
 def cpu_baseline(w, steps=1):
@@ -121,7 +126,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3, help="untimed compressed steps")
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=1)
+    ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's device copy of MIB MiB five times (a kernel of "
                          "known traffic for scaling profiler byte counters) and exit")
@@ -210,7 +215,12 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "worker pass",
                      "achieved": round(wk["GB_s"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(wk["GB_s"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic["bytes_per_launch"] if traffic else None,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
+                     "traffic_fetch": traffic["fetch_bytes_per_launch"] if traffic else None,
+                     "traffic_write": traffic["write_bytes_per_launch"] if traffic else None,
+                     "alg_bytes_per_launch": wk["alg_bytes"]},
         "step": {"alg_bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                  "frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "fp32_momentum_bytes": survey_b_alg(w),
