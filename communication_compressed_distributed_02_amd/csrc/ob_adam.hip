@@ -57,21 +57,18 @@ ob_status usable(ob_adam_t h) {
   return OB_OK;
 }
 
-// Launch `fn` bracketed by timing events when timing is on.
+// Run launcher `fn(t0, t1)`, handing it a pair of timing events when timing
+// is on (the events are taken from the dispatch packets themselves).
 template <typename F>
 hipError_t timed(ob_adam_t h, int kernel, F fn) {
   const int64_t cap = (int64_t)h->ev_kernel.size();
-  if (cap == 0) return fn();
+  if (cap == 0) return fn(nullptr, nullptr);
   if (h->ev_used >= cap) {
     h->ev_dropped += 1;
-    return fn();
+    return fn(nullptr, nullptr);
   }
   const int64_t i = h->ev_used;
-  hipError_t e = hipEventRecord(h->ev[2 * i], h->stream);
-  if (e != hipSuccess) return e;
-  e = fn();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(h->ev[2 * i + 1], h->stream);
+  hipError_t e = fn(h->ev[2 * i], h->ev[2 * i + 1]);
   if (e != hipSuccess) return e;
   h->ev_kernel[i] = kernel;
   h->ev_used = i + 1;
@@ -100,11 +97,18 @@ ob_status gather_grads(ob_adam_t h, const void* const* grads, int w0, int nw, ob
 ob_status finish_step(ob_adam_t h, float lr) {
   const ob::State& s = h->st;
   hipStream_t st = h->stream;
-  hipError_t e = timed(h, OB_K_WORKER_SCALE, [&] { return ob::launch_worker_scales(s, st); });
-  if (e == hipSuccess) e = timed(h, OB_K_SERVER, [&] { return ob::launch_server_pass(s, st); });
+  hipError_t e = timed(h, OB_K_WORKER_SCALE, [&](hipEvent_t a, hipEvent_t b) {
+    return ob::launch_worker_scales(s, st, a, b);
+  });
   if (e == hipSuccess)
-    e = timed(h, OB_K_SERVER_SCALE, [&] { return ob::launch_server_scales(s, st); });
-  if (e == hipSuccess) e = timed(h, OB_K_UPDATE, [&] { return ob::launch_update(s, lr, st); });
+    e = timed(h, OB_K_SERVER,
+              [&](hipEvent_t a, hipEvent_t b) { return ob::launch_server_pass(s, st, a, b); });
+  if (e == hipSuccess)
+    e = timed(h, OB_K_SERVER_SCALE,
+              [&](hipEvent_t a, hipEvent_t b) { return ob::launch_server_scales(s, st, a, b); });
+  if (e == hipSuccess)
+    e = timed(h, OB_K_UPDATE,
+              [&](hipEvent_t a, hipEvent_t b) { return ob::launch_update(s, lr, st, a, b); });
   if (e != hipSuccess) return fail(h, e);
   h->steps += 1;
   h->compressed += 1;
@@ -183,8 +187,9 @@ ob_status ob_adam_warmup_step(ob_adam_t h, const void* const* grads, float lr) {
   }
   const float bc1 = (float)(1.0 - p1);
   const float bc2 = (float)(1.0 - p2);
-  st = fail(h, timed(h, OB_K_WARMUP,
-                     [&] { return ob::launch_warmup(h->st, g, lr, bc1, bc2, h->stream); }));
+  st = fail(h, timed(h, OB_K_WARMUP, [&](hipEvent_t a, hipEvent_t b) {
+              return ob::launch_warmup(h->st, g, lr, bc1, bc2, h->stream, a, b);
+            }));
   if (st != OB_OK) return st;
   h->steps = t;
   h->warm += 1;
@@ -199,8 +204,8 @@ ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float l
   st = gather_grads(h, grads, 0, h->st.n, &g);
   if (st != OB_OK) return st;
   const bool m_bits = h->compressed > 0;
-  st = fail(h, timed(h, OB_K_WORKER, [&] {
-              return ob::launch_worker_pass(h->st, g, 0, h->st.n, m_bits, h->stream);
+  st = fail(h, timed(h, OB_K_WORKER, [&](hipEvent_t a, hipEvent_t b) {
+              return ob::launch_worker_pass(h->st, g, 0, h->st.n, m_bits, h->stream, a, b);
             }));
   if (st != OB_OK) return st;
   return finish_step(h, lr);
@@ -216,8 +221,8 @@ ob_status ob_adam_compress_worker(ob_adam_t h, int32_t worker, const void* grad)
   ob::GradPtrs g{};
   g.p[0] = grad;
   const bool m_bits = h->compressed > 0;
-  st = fail(h, timed(h, OB_K_WORKER, [&] {
-              return ob::launch_worker_pass(h->st, g, worker, 1, m_bits, h->stream);
+  st = fail(h, timed(h, OB_K_WORKER, [&](hipEvent_t a, hipEvent_t b) {
+              return ob::launch_worker_pass(h->st, g, worker, 1, m_bits, h->stream, a, b);
             }));
   if (st != OB_OK) return st;
   h->staged_open = true;

@@ -43,14 +43,17 @@ struct Layout {
 };
 Layout layout_for(int64_t d, int n);
 
+// t0 / t1: optional timing events recorded at the start of the first and the
+// end of the last dispatch of the launcher (null = untimed).
 hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1, float bc2,
-                         hipStream_t stream);
+                         hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw, bool m_bits,
-                              hipStream_t stream);
-hipError_t launch_worker_scales(const State& s, hipStream_t stream);
-hipError_t launch_server_pass(const State& s, hipStream_t stream);
-hipError_t launch_server_scales(const State& s, hipStream_t stream);
-hipError_t launch_update(const State& s, float lr, hipStream_t stream);
+                              hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_update(const State& s, float lr, hipStream_t stream, hipEvent_t t0,
+                         hipEvent_t t1);
 
 // Materialize derived fields for readback.
 hipError_t launch_error_out(const float* comp, const float* scales, int64_t L, int64_t offset,

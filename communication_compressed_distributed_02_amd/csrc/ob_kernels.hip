@@ -26,6 +26,7 @@
 //  - Sign words are read with scalar (uniform) loads and decoded with an
 //    inverse ballot: bit `lane` of a uniform 64-bit word selects +s or -s in
 //    one v_cndmask.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -552,6 +553,16 @@ __global__ void __launch_bounds__(kBlock)
   }
 }
 
+// Every launch goes through the runtime's extended launch so that timing
+// events, when requested, are taken from the dispatch packet itself (no extra
+// packets between kernels); with null events it is a plain launch.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                  hipEvent_t t0, hipEvent_t t1, Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, t0, t1, 0, args...);
+  return hipGetLastError();
+}
+
 unsigned grid_for(int64_t items, int64_t per_block, int64_t cap) {
   int64_t b = (items + per_block - 1) / per_block;
   if (b > cap) b = cap;
@@ -590,22 +601,22 @@ Layout layout_for(int64_t d, int n) {
 }
 
 hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1, float bc2,
-                         hipStream_t stream) {
+                         hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const float ob1 = 1.0f - s.beta1, ob2 = 1.0f - s.beta2;
-  const unsigned grid = grid_for(s.d, kBlock, 8192);
-#define OB_WARM(GT, NW)                                                                        \
-  warmup_kernel<GT, NW><<<grid, kBlock, 0, stream>>>(g, s.n, s.d, s.m, s.v, s.x, s.beta1, ob1, \
-                                                     s.beta2, ob2, bc1, bc2, lr, s.eps)
-#define OB_WARM_N(GT)      \
-  switch (s.n) {           \
-    case 1: OB_WARM(GT, 1); break;   \
-    case 2: OB_WARM(GT, 2); break;   \
-    case 4: OB_WARM(GT, 4); break;   \
-    case 8: OB_WARM(GT, 8); break;   \
-    case 16: OB_WARM(GT, 16); break; \
-    case 32: OB_WARM(GT, 32); break; \
-    case 64: OB_WARM(GT, 64); break; \
-    default: OB_WARM(GT, 0); break;  \
+  const dim3 grid(grid_for(s.d, kBlock, 8192));
+#define OB_WARM(GT, NW)                                                                     \
+  return launch(warmup_kernel<GT, NW>, grid, dim3(kBlock), stream, t0, t1, g, s.n, s.d, s.m, \
+                s.v, s.x, s.beta1, ob1, s.beta2, ob2, bc1, bc2, lr, s.eps)
+#define OB_WARM_N(GT)                \
+  switch (s.n) {                     \
+    case 1: OB_WARM(GT, 1);          \
+    case 2: OB_WARM(GT, 2);          \
+    case 4: OB_WARM(GT, 4);          \
+    case 8: OB_WARM(GT, 8);          \
+    case 16: OB_WARM(GT, 16);        \
+    case 32: OB_WARM(GT, 32);        \
+    case 64: OB_WARM(GT, 64);        \
+    default: OB_WARM(GT, 0);         \
   }
   if (s.grad_bf16) {
     OB_WARM_N(uint16_t)
@@ -614,33 +625,35 @@ hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1,
   }
 #undef OB_WARM_N
 #undef OB_WARM
-  return hipGetLastError();
 }
 
 hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw, bool m_bits,
-                              hipStream_t stream) {
+                              hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const float ob1 = 1.0f - s.beta1;
-  dim3 grid(grid_for(s.nseg, kWavesPerBlock * OB_WORKER_SEGS_PER_WAVE, OB_WORKER_BLOCKS_PER_ROW),
-            (unsigned)(nw * s.n));
-#define OB_WORK(GT, MB)                                                                          \
-  worker_kernel<GT, MB><<<grid, kBlock, 0, stream>>>(g, w0, s.d, s.L, s.n, s.nseg, s.words, s.m, \
-                                                     s.sbits, s.sscale, s.c, s.wscale, s.wbits,  \
-                                                     s.wpart, s.beta1, ob1)
+  const dim3 grid(grid_for(s.nseg, kWavesPerBlock * OB_WORKER_SEGS_PER_WAVE, OB_WORKER_BLOCKS_PER_ROW),
+                  (unsigned)(nw * s.n));
+#define OB_WORK(GT, MB)                                                                        \
+  return launch(worker_kernel<GT, MB>, grid, dim3(kBlock), stream, t0, t1, g, w0, s.d, s.L, s.n, \
+                s.nseg, s.words, (const float*)s.m, (const uint64_t*)s.sbits,                    \
+                (const float*)s.sscale, s.c, (const float*)s.wscale, s.wbits, s.wpart, s.beta1,  \
+                ob1)
   if (s.grad_bf16) {
-    if (m_bits) OB_WORK(uint16_t, true); else OB_WORK(uint16_t, false);
-  } else {
-    if (m_bits) OB_WORK(float, true); else OB_WORK(float, false);
+    if (m_bits) OB_WORK(uint16_t, true);
+    OB_WORK(uint16_t, false);
   }
+  if (m_bits) OB_WORK(float, true);
+  OB_WORK(float, false);
 #undef OB_WORK
-  return hipGetLastError();
 }
 
 // Scales of `rows` rows of segment partials (nseg per row) into scale_out:
 // fold aligned groups of kGroup until at most kGroup values remain per row,
 // then the last fold and the scale.  `fold` holds rows *
-// fold_doubles_per_row(nseg) doubles.
+// fold_doubles_per_row(nseg) doubles.  t0 is taken at the first launch, t1
+// at the last.
 static hipError_t launch_scales(const double* part, int64_t nseg, int64_t L, int rows,
-                                double* fold, float* scale_out, hipStream_t stream) {
+                                double* fold, float* scale_out, hipStream_t stream,
+                                hipEvent_t t0, hipEvent_t t1) {
   const double* cur = part;
   int64_t cnt = nseg;
   double* out = fold;
@@ -649,66 +662,65 @@ static hipError_t launch_scales(const double* part, int64_t nseg, int64_t L, int
     while (width < cnt) width <<= 1;
     if (width <= kGroup) break;
     const int64_t ngroups = width / kGroup;
-    fold_groups_kernel<<<dim3((unsigned)ngroups, (unsigned)rows), kBlock, 0, stream>>>(
-        cur, cnt, ngroups, out);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch(fold_groups_kernel, dim3((unsigned)ngroups, (unsigned)rows),
+                          dim3(kBlock), stream, t0, nullptr, cur, cnt, ngroups, out);
     if (e != hipSuccess) return e;
+    t0 = nullptr;
     cur = out;
     cnt = ngroups;
     out += (int64_t)rows * ngroups;
   }
-  scale_kernel<<<rows, kBlock, 0, stream>>>(cur, cnt, L, scale_out);
-  return hipGetLastError();
+  return launch(scale_kernel, dim3((unsigned)rows), dim3(kBlock), stream, t0, t1, cur, cnt, L,
+                scale_out);
 }
 
-hipError_t launch_worker_scales(const State& s, hipStream_t stream) {
-  return launch_scales(s.wpart, s.nseg, s.L, s.n * s.n, s.fold, s.wscale, stream);
+hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  return launch_scales(s.wpart, s.nseg, s.L, s.n * s.n, s.fold, s.wscale, stream, t0, t1);
 }
 
-hipError_t launch_server_pass(const State& s, hipStream_t stream) {
-  dim3 grid(grid_for(s.nseg, kWavesPerBlock, OB_SERVER_BLOCKS_PER_ROW), (unsigned)s.n);
-#define OB_SRV(NW)                                                                        \
-  server_kernel<NW><<<grid, kBlock, 0, stream>>>(s.L, s.n, s.nseg, s.words, s.wbits,      \
-                                                 s.wscale, s.u, s.sscale, s.sbits, s.spart)
+hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const dim3 grid(grid_for(s.nseg, kWavesPerBlock, OB_SERVER_BLOCKS_PER_ROW), (unsigned)s.n);
+#define OB_SRV(NW)                                                                             \
+  return launch(server_kernel<NW>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n, s.nseg,       \
+                s.words, (const uint64_t*)s.wbits, (const float*)s.wscale, s.u,                 \
+                (const float*)s.sscale, s.sbits, s.spart)
   switch (s.n) {
-    case 1: OB_SRV(1); break;
-    case 2: OB_SRV(2); break;
-    case 4: OB_SRV(4); break;
-    case 8: OB_SRV(8); break;
-    case 16: OB_SRV(16); break;
-    case 32: OB_SRV(32); break;
-    case 64: OB_SRV(64); break;
-    default: OB_SRV(0); break;
+    case 1: OB_SRV(1);
+    case 2: OB_SRV(2);
+    case 4: OB_SRV(4);
+    case 8: OB_SRV(8);
+    case 16: OB_SRV(16);
+    case 32: OB_SRV(32);
+    case 64: OB_SRV(64);
+    default: OB_SRV(0);
   }
 #undef OB_SRV
-  return hipGetLastError();
 }
 
-hipError_t launch_server_scales(const State& s, hipStream_t stream) {
-  return launch_scales(s.spart, s.nseg, s.L, s.n, s.fold, s.sscale, stream);
+hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  return launch_scales(s.spart, s.nseg, s.L, s.n, s.fold, s.sscale, stream, t0, t1);
 }
 
-hipError_t launch_update(const State& s, float lr, hipStream_t stream) {
+hipError_t launch_update(const State& s, float lr, hipStream_t stream, hipEvent_t t0,
+                         hipEvent_t t1) {
   const int64_t groups = (s.words + kSegRows - 1) / kSegRows;
-  update_kernel<<<grid_for(groups, kWavesPerBlock, OB_UPDATE_BLOCKS), kBlock, 0, stream>>>(
-      s.words, s.L, s.sbits, s.sscale, s.v, s.x, lr, s.eps);
-  return hipGetLastError();
+  return launch(update_kernel, dim3(grid_for(groups, kWavesPerBlock, OB_UPDATE_BLOCKS)),
+                dim3(kBlock), stream, t0, t1, s.words, s.L, (const uint64_t*)s.sbits,
+                (const float*)s.sscale, (const float*)s.v, s.x, lr, s.eps);
 }
 
 hipError_t launch_error_out(const float* comp, const float* scales, int64_t L, int64_t offset,
                             int64_t count, float* dst, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
-  error_out_kernel<<<grid_for(count, kBlock, 16384), kBlock, 0, stream>>>(comp, scales, L, offset,
-                                                                          count, dst);
-  return hipGetLastError();
+  return launch(error_out_kernel, dim3(grid_for(count, kBlock, 16384)), dim3(kBlock), stream,
+                nullptr, nullptr, comp, scales, L, offset, count, dst);
 }
 
 hipError_t launch_decompress_out(const uint64_t* bits, const float* scales, int64_t L,
                                  int64_t offset, int64_t count, float* dst, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
-  decompress_out_kernel<<<grid_for(count, kBlock, 16384), kBlock, 0, stream>>>(bits, scales, L,
-                                                                               offset, count, dst);
-  return hipGetLastError();
+  return launch(decompress_out_kernel, dim3(grid_for(count, kBlock, 16384)), dim3(kBlock), stream,
+                nullptr, nullptr, bits, scales, L, offset, count, dst);
 }
 
 }  // namespace ob

@@ -158,11 +158,13 @@ enum {
   OB_NUM_KERNELS = 6
 };
 
-/* Per-kernel timing.  With max_launches > 0, every later kernel launch of a
- * step is bracketed by a pair of HIP events recorded on the handle's stream,
- * up to max_launches launches (later ones are counted as dropped); 0 turns
- * timing off and releases the events.  The events are host-side runtime
- * objects (no device memory is allocated). */
+/* Per-kernel timing.  With max_launches > 0, each later kernel launch (for a
+ * kernel made of several dispatches: from the first to the last) gets a pair
+ * of HIP events taken from its dispatch packets on the handle's stream (the
+ * runtime's extended launch; no extra packets between kernels), up to
+ * max_launches launches (later ones are counted as dropped); 0 turns timing
+ * off and releases the events.  The events are host-side runtime objects (no
+ * device memory is allocated). */
 ob_status ob_adam_set_timing(ob_adam_t h, int32_t max_launches);
 
 /* Synchronize the stream, then return for each kernel (index OB_K_*) the
