@@ -105,18 +105,74 @@ def cpu_baseline(w, steps=1):
             "s_per_step_extrapolated": per_step}
 
 
-def copy_calibration(mib):
-    """A plain copy of known size: each dispatch reads and writes mib MiB."""
+PROBE_LIB = os.path.join(ROOT, "communication_compressed_distributed_02_amd", "libob_probe.so")
+PROBE_KINDS = {"mix": 0, "copy": 1, "read": 2, "write": 3}
+
+
+def probe_lib():
+    import ctypes
+    import torch  # noqa: F401  (torch's HIP runtime first)
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError("libob_probe.so is not built: run __graft_entry__.build()")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.ob_probe_run.restype = ctypes.c_int
+    lib.ob_probe_run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_void_p]
+    return lib
+
+
+def run_probe(lib, kind, a, b, n):
     import torch
+    rc = lib.ob_probe_run(PROBE_KINDS[kind], a.data_ptr() if a is not None else None,
+                          b.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError("ob_probe_run(%s) failed: %d" % (kind, rc))
+
+
+def copy_calibration(mib):
+    """Plain streaming kernels of known size (mib MiB each): copy, read-only and
+    write-only, three dispatches each, for scaling profiler byte counters."""
+    import torch
+    lib = probe_lib()
     n = mib * 1024 * 1024 // 4
+    n -= n % 4096
     x = torch.ones(n, dtype=torch.float32, device="cuda:0")
     y = torch.empty_like(x)
     torch.cuda.synchronize()
-    for _ in range(5):
-        y.copy_(x)
+    for kind, a in (("copy", x), ("read", x), ("write", None)):
+        for _ in range(3):
+            run_probe(lib, kind, a, y, n)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
-                      "dispatches": 5}), flush=True)
+    print(json.dumps({"calibration_bytes": 4 * n, "copy": "reads and writes 4n",
+                      "read": "reads 4n", "write": "writes 4n", "dispatches_each": 3}), flush=True)
+
+
+def stream_ceilings(n, reps=5):
+    """GB/s of the probes over n elements on this device: the worker pass's
+    access mix (6 B read + 4 B written per element), copy, read-only and
+    write-only, with the step's own wave-row mapping and non-temporal hints."""
+    import torch
+    lib = probe_lib()
+    n -= n % 4096
+    g = torch.zeros(n, dtype=torch.int16, device="cuda:0")
+    c = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    c2 = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    out = {}
+    for kind, a, b, nbytes in (("mix", g, c, 10 * n), ("copy", c, c2, 8 * n),
+                               ("read", c, c2, 4 * n), ("write", None, c2, 4 * n)):
+        for _ in range(2):
+            run_probe(lib, kind, a, b, n)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run_probe(lib, kind, a, b, n)
+        e1.record()
+        torch.cuda.synchronize()
+        out[kind + "_GB_s"] = round(nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del g, c, c2
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -263,8 +319,13 @@ def main():
                  "timing_launches_dropped": dropped},
         "kernels": kernels,
     }
-    del grads, opt
+    del grads, ring_grads, opt
     torch.cuda.empty_cache()
+    ceil = stream_ceilings(w.n * w.d if not w.staged else w.d)
+    ceil["note"] = ("probe kernels with the worker pass's mapping over as many elements as one "
+                    "launch of it; mix = its 6 B read + 4 B written per element")
+    ceil["worker_frac_of_mix"] = round(wk["GB_s"] / ceil["mix_GB_s"], 4)
+    result["ceilings"] = ceil
     if not a.no_cpu_baseline:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, a.cpu_steps)

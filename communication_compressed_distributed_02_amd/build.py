@@ -19,6 +19,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
          "-fPIC", "-shared", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+PROBE_LIB = os.path.join(PKG, "libob_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "ob_probe.hip")]
+
+
 def build(extra_flags=(), out=LIB):
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + FLAGS + list(extra_flags) + SOURCES + ["-o", tmp]
@@ -27,5 +31,14 @@ def build(extra_flags=(), out=LIB):
     return out
 
 
+def build_probe(out=PROBE_LIB):
+    """Streaming probes used by bench.py for ceilings and counter calibration."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC] + FLAGS + PROBE_SOURCES + ["-o", tmp])
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_probe())

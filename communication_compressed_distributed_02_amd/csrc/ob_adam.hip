@@ -76,6 +76,8 @@ hipError_t timed(ob_adam_t h, int kernel, F fn) {
 }
 
 void release_events(ob_adam_t h) {
+  // recorded events may still be pending on the stream: let them complete
+  if (h->ev_used > 0) (void)hipStreamSynchronize(h->stream);
   for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
   h->ev.clear();
   h->ev_kernel.clear();
@@ -310,6 +312,12 @@ ob_status ob_adam_set_state(ob_adam_t h, int32_t field, int64_t offset, int64_t 
   if (src_device == nullptr) return OB_ERR_ARG;
   return fail(h, hipMemcpyAsync(dst + offset, src_device, sizeof(float) * (size_t)count,
                                 hipMemcpyDeviceToDevice, h->stream));
+}
+
+ob_status ob_adam_params(ob_adam_t h, float** x_device) {
+  if (h == nullptr || x_device == nullptr) return OB_ERR_ARG;
+  *x_device = h->st.x;
+  return OB_OK;
 }
 
 ob_status ob_adam_step_count(ob_adam_t h, int64_t* steps, int64_t* compressed_steps) {

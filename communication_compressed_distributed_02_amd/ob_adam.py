@@ -21,7 +21,8 @@ OB_GRAD_F32, OB_GRAD_BF16 = 0, 1
 
 EXPORTED = ("ob_adam_workspace_bytes", "ob_adam_init", "ob_adam_warmup_step",
             "ob_adam_compressed_step", "ob_adam_compress_worker", "ob_adam_compressed_finish",
-            "ob_adam_get_state", "ob_adam_set_state", "ob_adam_step_count", "ob_adam_set_timing",
+            "ob_adam_get_state", "ob_adam_set_state", "ob_adam_params", "ob_adam_step_count",
+            "ob_adam_set_timing",
             "ob_adam_kernel_times", "ob_adam_destroy", "ob_status_str")
 KERNELS = ("warmup", "worker", "worker_scale", "server", "server_scale", "update")
 
@@ -53,6 +54,7 @@ def _load(path=LIB_PATH):
         "ob_adam_compressed_finish": [P, F],
         "ob_adam_get_state": [P, I32, I32, I64, I64, P],
         "ob_adam_set_state": [P, I32, I64, I64, P],
+        "ob_adam_params": [P, ctypes.POINTER(P)],
         "ob_adam_step_count": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "ob_adam_set_timing": [P, I32],
         "ob_adam_kernel_times": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64),
@@ -124,6 +126,12 @@ def ob_adam_get_state(h, field, worker, offset, count, dst_ptr):
 
 def ob_adam_set_state(h, field, offset, count, src_ptr):
     _check(_lib.ob_adam_set_state(h, field, offset, count, src_ptr), "ob_adam_set_state")
+
+
+def ob_adam_params(h):
+    p = ctypes.c_void_p(0)
+    _check(_lib.ob_adam_params(h, ctypes.byref(p)), "ob_adam_params")
+    return p.value
 
 
 def ob_adam_step_count(h):
@@ -209,6 +217,13 @@ class OneBitAdam:
         if src.dtype != torch.float32 or not src.is_contiguous():
             raise ValueError("source must be a contiguous float32 tensor")
         ob_adam_set_state(self.h, field, offset, src.numel(), src.data_ptr())
+
+    def params_view(self):
+        """fp32[d] tensor aliasing the library's parameters x (no copy)."""
+        off = ob_adam_params(self.h) - self.workspace.data_ptr()
+        if off < 0 or off + 4 * self.d > self.ws_bytes:
+            raise RuntimeError("parameter buffer outside the workspace")
+        return self.workspace[off:off + 4 * self.d].view(torch.float32)
 
     @property
     def steps(self):

@@ -144,6 +144,12 @@ ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t 
 ob_status ob_adam_set_state(ob_adam_t h, int32_t field, int64_t offset, int64_t count,
                             const void* src_device);
 
+/* Device address of the parameters x (fp32[d], contiguous, inside the
+ * caller's workspace), so that a caller can keep its parameter tensors as
+ * views of it instead of copying them in and out every step.  The caller may
+ * read and write x between steps, ordered on the handle's stream. */
+ob_status ob_adam_params(ob_adam_t h, float** x_device);
+
 /* Steps taken so far (warm-up and compressed) and compressed steps taken. */
 ob_status ob_adam_step_count(ob_adam_t h, int64_t* steps, int64_t* compressed_steps);
 
