@@ -252,6 +252,9 @@ ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t 
   const bool per_worker =
       field == OB_E_WORKER || field == OB_BITS_WORKER || field == OB_SCALE_WORKER;
   if (per_worker && (worker < 0 || worker >= s.n)) return OB_ERR_ARG;
+  // mid-way through a worker-at-a-time step the compressed workers' slabs
+  // already belong to the new step while the scales still belong to the old
+  if (h->staged_open && (field == OB_E_WORKER || field == OB_BITS_WORKER)) return OB_ERR_PHASE;
   int64_t size;
   switch (field) {
     case OB_X: case OB_M: case OB_V: case OB_E_WORKER: case OB_E_SERVER: size = s.d; break;

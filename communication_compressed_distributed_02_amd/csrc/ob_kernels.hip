@@ -421,6 +421,65 @@ __device__ __forceinline__ void server_average_segment(const uint64_t* __restric
   for (int r = 0; r < kSegRows; ++r) avg[r] = stack[LEVELS - 1][r] / (float)NW;
 }
 
+// Many workers (NW >= 32, a power of two): R rows at a time, workers in
+// batches of 4 (one burst of four 64-byte scalar loads per batch, the 4-worker
+// subtree formed in registers), batches folded into per-row stacks in batch
+// order -- again exactly the pairwise-by-levels sum -- with the stack levels as
+// compile-time indices under a uniform run-time batch loop, which keeps the
+// register footprint (and so the occupancy) independent of NW.
+template <int NW, int R>
+__device__ __forceinline__ void server_average_rows(const uint64_t* __restrict__ wbits,
+                                                    int64_t words, int64_t wbase,
+                                                    const float* __restrict__ wscale, int n,
+                                                    int j, float* avg) {
+  constexpr int B = 4;
+  constexpr int NB = NW / B;
+  constexpr int LB = NB == 4 ? 3 : NB == 8 ? 4 : NB == 16 ? 5 : 6;  // log2(NB) + 1
+  static_assert(NW >= 16 && NW <= 128 && (NW & (NW - 1)) == 0, "power of two, 16..128");
+  // (used from NW = 32 on: at 16 workers the fully unrolled segment path is faster)
+  float stack[LB][R];
+#pragma unroll 1
+  for (int b = 0; b < NB; ++b) {
+    float s[B];
+    uint64_t wd[B][R];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int w = b * B + q;
+      s[q] = wscale[w * n + j];
+      const uint64_t* __restrict__ p = wbits + (int64_t)w * words + wbase;
+#pragma unroll
+      for (int r = 0; r < R; ++r) wd[q][r] = p[r];
+    }
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float a0 = signed_scale(wd[0][r], s[0]);
+      const float a1 = signed_scale(wd[1][r], s[1]);
+      const float a2 = signed_scale(wd[2][r], s[2]);
+      const float a3 = signed_scale(wd[3][r], s[3]);
+      v[r] = (a0 + a1) + (a2 + a3);
+    }
+    int x = b;
+    bool carry = true;
+#pragma unroll
+    for (int lvl = 0; lvl < LB; ++lvl) {
+      if (carry) {
+        if (x & 1) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) v[r] = stack[lvl][r] + v[r];
+          x >>= 1;
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; ++r) stack[lvl][r] = v[r];
+          carry = false;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) avg[r] = stack[LB - 1][r] / (float)NW;
+}
+
 template <int NW>
 __global__ void __launch_bounds__(kBlock)
     server_kernel(int64_t L, int n, int64_t nseg, int64_t words,
@@ -429,10 +488,13 @@ __global__ void __launch_bounds__(kBlock)
                   uint64_t* __restrict__ sbits, double* __restrict__ spart) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.y;
-  float ws[NW > 0 ? NW : kMaxWorkersPerLaunch];
+  // per-chunk worker scales in registers for the small-NW paths; the
+  // many-worker path reads them per batch instead
+  constexpr int WS = NW >= 32 ? 1 : (NW > 0 ? NW : kMaxWorkersPerLaunch);
+  float ws[WS];
   const int nw = NW > 0 ? NW : n;
 #pragma unroll
-  for (int w = 0; w < (NW > 0 ? NW : kMaxWorkersPerLaunch); ++w)
+  for (int w = 0; w < WS; ++w)
     if (w < nw) ws[w] = wscale[w * n + j];
   const float sp = sscale_prev[j];
   const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
@@ -451,7 +513,13 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
         for (int r = 0; r < kSegRows; ++r) up[r] = ld_stream(u + base + 64 * r + lane);
         float avg[kSegRows];
-        server_average_segment<NW>(wbits, words, wbase, ws, avg);
+        if constexpr (NW >= 32) {
+          server_average_rows<NW, kSegRows / 2>(wbits, words, wbase, wscale, n, j, avg);
+          server_average_rows<NW, kSegRows / 2>(wbits, words, wbase + kSegRows / 2, wscale, n,
+                                                j, avg + kSegRows / 2);
+        } else {
+          server_average_segment<NW>(wbits, words, wbase, ws, avg);
+        }
 #pragma unroll
         for (int r = 0; r < kSegRows; ++r) {
           const float e = up[r] - (up[r] >= 0.0f ? sp : -sp);
@@ -471,7 +539,12 @@ __global__ void __launch_bounds__(kBlock)
       const int64_t k = base + 64 * r + lane;
       const float up = u[k];
       const float e = up - (up >= 0.0f ? sp : -sp);
-      const float a = worker_average<NW>(wbits, words, wbase + r, ws, n);
+      float a;
+      if constexpr (NW >= 32) {
+        server_average_rows<NW, 1>(wbits, words, wbase + r, wscale, n, j, &a);
+      } else {
+        a = worker_average<NW>(wbits, words, wbase + r, ws, n);
+      }
       const float uv = a + e;
       u[k] = uv;
       const uint64_t word = __ballot(uv >= 0.0f);

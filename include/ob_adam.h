@@ -135,7 +135,9 @@ ob_status ob_adam_compressed_finish(ob_adam_t h, float lr);
  * OB_E_WORKER, OB_BITS_WORKER and OB_SCALE_WORKER of worker `worker`) into
  * device memory `dst_device`.  Derived fields (errors, decompressed momentum)
  * are materialized by a kernel.  Enqueued on the handle's stream; the range
- * must lie inside the field (OB_ERR_ARG otherwise). */
+ * must lie inside the field (OB_ERR_ARG otherwise).  OB_E_WORKER and
+ * OB_BITS_WORKER are refused (OB_ERR_PHASE) while a worker-at-a-time step is
+ * open, as they would mix the old and the new step. */
 ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t offset,
                             int64_t count, void* dst_device);
 

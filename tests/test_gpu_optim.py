@@ -22,14 +22,6 @@ def _gpu():
 SHAPES = [(30, 17), (5,), (64, 64), (1,), (3, 3, 7), (200,), (128, 33)]
 
 
-def test_flat_layout_pads_each_tensor_and_the_total():
-    from communication_compressed_distributed_02_amd.optim import flat_layout
-    offs, d = flat_layout([510, 5, 4096, 1], 4)
-    assert offs == [0, 512, 576, 4672]
-    assert d == 4 * 64 * 19  # 4736 rounded up to a multiple of 256
-    assert all(o % 64 == 0 for o in offs)
-
-
 def test_ragged_params_match_oracle_and_copy_nothing():
     import torch
     from communication_compressed_distributed_02_amd.optim import OneBitAdamOptimizer

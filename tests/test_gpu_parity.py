@@ -141,6 +141,10 @@ def test_phase_rules_and_ranges():
     with pytest.raises(ob.ObAdamError) as e:
         opt.compress_worker(2, g[2])
     assert e.value.status == ob.OB_ERR_PHASE
+    for f in (ob.OB_E_WORKER, ob.OB_BITS_WORKER):  # half-updated while the step is open
+        with pytest.raises(ob.ObAdamError) as e:
+            opt.get(f, 2, 0, 4)
+        assert e.value.status == ob.OB_ERR_PHASE
     with pytest.raises(ob.ObAdamError) as e:
         opt.compressed_finish(1e-3)
     assert e.value.status == ob.OB_ERR_PHASE
