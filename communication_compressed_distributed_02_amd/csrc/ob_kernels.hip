@@ -430,8 +430,7 @@ __device__ __forceinline__ void server_average_segment(const uint64_t* __restric
 template <int NW, int R>
 __device__ __forceinline__ void server_average_rows(const uint64_t* __restrict__ wbits,
                                                     int64_t words, int64_t wbase,
-                                                    const float* __restrict__ wscale, int n,
-                                                    int j, float* avg) {
+                                                    const float* sws, float* avg) {
   constexpr int B = 4;
   constexpr int NB = NW / B;
   constexpr int LB = NB == 4 ? 3 : NB == 8 ? 4 : NB == 16 ? 5 : 6;  // log2(NB) + 1
@@ -445,7 +444,7 @@ __device__ __forceinline__ void server_average_rows(const uint64_t* __restrict__
 #pragma unroll
     for (int q = 0; q < B; ++q) {
       const int w = b * B + q;
-      s[q] = wscale[w * n + j];
+      s[q] = sws[w];  // this chunk's worker scales, staged in LDS
       const uint64_t* __restrict__ p = wbits + (int64_t)w * words + wbase;
 #pragma unroll
       for (int r = 0; r < R; ++r) wd[q][r] = p[r];
@@ -496,6 +495,11 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
   for (int w = 0; w < WS; ++w)
     if (w < nw) ws[w] = wscale[w * n + j];
+  __shared__ float sws[NW >= 32 ? NW : 1];
+  if constexpr (NW >= 32) {
+    if ((int)threadIdx.x < NW) sws[threadIdx.x] = wscale[threadIdx.x * n + j];
+    __syncthreads();
+  }
   const float sp = sscale_prev[j];
   const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
   for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); s < nseg;
@@ -514,9 +518,9 @@ __global__ void __launch_bounds__(kBlock)
         for (int r = 0; r < kSegRows; ++r) up[r] = ld_stream(u + base + 64 * r + lane);
         float avg[kSegRows];
         if constexpr (NW >= 32) {
-          server_average_rows<NW, kSegRows / 2>(wbits, words, wbase, wscale, n, j, avg);
-          server_average_rows<NW, kSegRows / 2>(wbits, words, wbase + kSegRows / 2, wscale, n,
-                                                j, avg + kSegRows / 2);
+          server_average_rows<NW, kSegRows / 2>(wbits, words, wbase, sws, avg);
+          server_average_rows<NW, kSegRows / 2>(wbits, words, wbase + kSegRows / 2, sws,
+                                                avg + kSegRows / 2);
         } else {
           server_average_segment<NW>(wbits, words, wbase, ws, avg);
         }
@@ -541,7 +545,7 @@ __global__ void __launch_bounds__(kBlock)
       const float e = up - (up >= 0.0f ? sp : -sp);
       float a;
       if constexpr (NW >= 32) {
-        server_average_rows<NW, 1>(wbits, words, wbase + r, wscale, n, j, &a);
+        server_average_rows<NW, 1>(wbits, words, wbase + r, sws, &a);
       } else {
         a = worker_average<NW>(wbits, words, wbase + r, ws, n);
       }

@@ -37,6 +37,9 @@ CASES = [
     ("n8_bf16", 8 * 41152, 8, True, 1e-3, 2, 4),
     ("n16_short_chunks", 16 * 448, 16, False, 1e-3, 2, 3),
     ("n64_workers", 64 * 1088, 64, False, 1e-3, 2, 3),
+    ("n32_workers", 32 * 2112, 32, True, 1e-3, 2, 3),
+    ("n6_generic", 6 * 1152, 6, False, 1e-2, 1, 3),
+    ("n7_generic", 7 * 1088, 7, False, 1e-2, 1, 3),
     ("n2_two_fold_groups", 2 * 614976, 2, False, 1e-2, 1, 3),
     ("n1_eight_fold_groups", 3072064, 1, True, 1e-3, 1, 2),
 ]
