@@ -129,16 +129,13 @@ ob_status ob_adam_workspace_bytes(const ob_adam_config* cfg, uint64_t* bytes) {
   return OB_OK;
 }
 
-ob_status ob_adam_init(const ob_adam_config* cfg, void* workspace, uint64_t ws_bytes,
-                       const float* x0, void* stream, ob_adam_t* out) {
-  ob_status st = check_config(cfg);
-  if (st != OB_OK) return st;
-  if (out == nullptr) return OB_ERR_ARG;
+namespace {
+
+// A handle over `workspace` (validated by the caller); nullptr if out of memory.
+ob_adam_handle* make_handle(const ob_adam_config* cfg, void* workspace, void* stream) {
   const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers);
-  if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0 || ws_bytes < l.total)
-    return OB_ERR_WORKSPACE;
   ob_adam_handle* h = new (std::nothrow) ob_adam_handle();
-  if (h == nullptr) return OB_ERR_ARG;
+  if (h == nullptr) return nullptr;
   char* base = (char*)workspace;
   ob::State& s = h->st;
   s.d = cfg->d;
@@ -163,6 +160,29 @@ ob_status ob_adam_init(const ob_adam_config* cfg, void* workspace, uint64_t ws_b
   s.wscale = (float*)(base + l.wscale);
   s.sscale = (float*)(base + l.sscale);
   h->stream = (hipStream_t)stream;
+  return h;
+}
+
+ob_status check_workspace(const ob_adam_config* cfg, void* workspace, uint64_t ws_bytes) {
+  const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers);
+  if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0 || ws_bytes < l.total)
+    return OB_ERR_WORKSPACE;
+  return OB_OK;
+}
+
+}  // namespace
+
+ob_status ob_adam_init(const ob_adam_config* cfg, void* workspace, uint64_t ws_bytes,
+                       const float* x0, void* stream, ob_adam_t* out) {
+  ob_status st = check_config(cfg);
+  if (st != OB_OK) return st;
+  if (out == nullptr) return OB_ERR_ARG;
+  st = check_workspace(cfg, workspace, ws_bytes);
+  if (st != OB_OK) return st;
+  ob_adam_handle* h = make_handle(cfg, workspace, stream);
+  if (h == nullptr) return OB_ERR_ARG;
+  const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers);
+  const ob::State& s = h->st;
   hipError_t e = hipMemsetAsync(workspace, 0, l.total, h->stream);
   if (e == hipSuccess && x0 != nullptr)
     e = hipMemcpyAsync(s.x, x0, sizeof(float) * (size_t)s.d, hipMemcpyDeviceToDevice, h->stream);
@@ -171,6 +191,36 @@ ob_status ob_adam_init(const ob_adam_config* cfg, void* workspace, uint64_t ws_b
     return OB_ERR_HIP;
   }
   *out = h;
+  return OB_OK;
+}
+
+ob_status ob_adam_attach(const ob_adam_config* cfg, void* workspace, uint64_t ws_bytes,
+                         const ob_adam_counters* counters, void* stream, ob_adam_t* out) {
+  ob_status st = check_config(cfg);
+  if (st != OB_OK) return st;
+  if (out == nullptr || counters == nullptr) return OB_ERR_ARG;
+  const ob_adam_counters& c = *counters;
+  if (c.steps < 0 || c.compressed_steps < 0 || c.warmup_steps < 0 ||
+      c.steps != c.compressed_steps + c.warmup_steps ||
+      (c.compressed_steps > 0 && c.warmup_steps == 0))
+    return OB_ERR_ARG;
+  st = check_workspace(cfg, workspace, ws_bytes);
+  if (st != OB_OK) return st;
+  ob_adam_handle* h = make_handle(cfg, workspace, stream);
+  if (h == nullptr) return OB_ERR_ARG;
+  h->steps = c.steps;
+  h->compressed = c.compressed_steps;
+  h->warm = c.warmup_steps;
+  *out = h;
+  return OB_OK;
+}
+
+ob_status ob_adam_get_counters(ob_adam_t h, ob_adam_counters* out) {
+  if (h == nullptr || out == nullptr) return OB_ERR_ARG;
+  if (h->staged_open) return OB_ERR_PHASE;
+  out->steps = h->steps;
+  out->compressed_steps = h->compressed;
+  out->warmup_steps = h->warm;
   return OB_OK;
 }
 

@@ -22,7 +22,7 @@ OB_GRAD_F32, OB_GRAD_BF16 = 0, 1
 EXPORTED = ("ob_adam_workspace_bytes", "ob_adam_init", "ob_adam_warmup_step",
             "ob_adam_compressed_step", "ob_adam_compress_worker", "ob_adam_compressed_finish",
             "ob_adam_get_state", "ob_adam_set_state", "ob_adam_params", "ob_adam_step_count",
-            "ob_adam_set_timing",
+            "ob_adam_get_counters", "ob_adam_attach", "ob_adam_set_timing",
             "ob_adam_kernel_times", "ob_adam_destroy", "ob_status_str")
 KERNELS = ("warmup", "worker", "worker_scale", "server", "server_scale", "update")
 
@@ -37,6 +37,11 @@ class ob_adam_config(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int64), ("n_workers", ctypes.c_int32),
                 ("grad_dtype", ctypes.c_int32), ("beta1", ctypes.c_float),
                 ("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
+class ob_adam_counters(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int64), ("compressed_steps", ctypes.c_int64),
+                ("warmup_steps", ctypes.c_int64)]
 
 
 def _load(path=LIB_PATH):
@@ -55,6 +60,8 @@ def _load(path=LIB_PATH):
         "ob_adam_get_state": [P, I32, I32, I64, I64, P],
         "ob_adam_set_state": [P, I32, I64, I64, P],
         "ob_adam_params": [P, ctypes.POINTER(P)],
+        "ob_adam_get_counters": [P, ctypes.POINTER(ob_adam_counters)],
+        "ob_adam_attach": [cfgp, P, U64, ctypes.POINTER(ob_adam_counters), P, ctypes.POINTER(P)],
         "ob_adam_step_count": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "ob_adam_set_timing": [P, I32],
         "ob_adam_kernel_times": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64),
@@ -134,6 +141,20 @@ def ob_adam_params(h):
     return p.value
 
 
+def ob_adam_get_counters(h):
+    c = ob_adam_counters()
+    _check(_lib.ob_adam_get_counters(h, ctypes.byref(c)), "ob_adam_get_counters")
+    return (c.steps, c.compressed_steps, c.warmup_steps)
+
+
+def ob_adam_attach(cfg, workspace_ptr, ws_bytes, counters, stream_ptr):
+    c = ob_adam_counters(*counters)
+    h = ctypes.c_void_p(0)
+    _check(_lib.ob_adam_attach(ctypes.byref(cfg), workspace_ptr, ws_bytes, ctypes.byref(c),
+                               stream_ptr, ctypes.byref(h)), "ob_adam_attach")
+    return h.value
+
+
 def ob_adam_step_count(h):
     a, b = ctypes.c_int64(0), ctypes.c_int64(0)
     _check(_lib.ob_adam_step_count(h, ctypes.byref(a), ctypes.byref(b)), "ob_adam_step_count")
@@ -167,13 +188,27 @@ class OneBitAdam:
     """A handle plus the torch-allocated workspace it lives in."""
 
     def __init__(self, d, n_workers, grad_dtype=OB_GRAD_F32, beta1=0.9, beta2=0.999, eps=1e-8,
-                 x0=None, device="cuda", stream=None):
+                 x0=None, device="cuda", stream=None, checkpoint=None):
+        """checkpoint: (workspace bytes as a uint8 tensor, counters) from
+        checkpoint() of a handle with the same configuration; the state is
+        copied into a fresh workspace and attached instead of initialized."""
         self.cfg = make_config(d, n_workers, grad_dtype, beta1, beta2, eps)
         self.d, self.n = d, n_workers
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         self.ws_bytes = ob_adam_workspace_bytes(self.cfg)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        if checkpoint is not None:
+            data, counters = checkpoint
+            if data.numel() != self.ws_bytes:
+                raise ValueError("checkpoint of %d bytes, workspace needs %d"
+                                 % (data.numel(), self.ws_bytes))
+            with torch.cuda.stream(self.stream):
+                self.workspace.copy_(data)
+            self.stream.synchronize()
+            self.h = ob_adam_attach(self.cfg, self.workspace.data_ptr(), self.ws_bytes, counters,
+                                    self.stream.cuda_stream)
+            return
         x0p = None
         if x0 is not None:
             if x0.dtype != torch.float32 or x0.numel() != d or not x0.is_contiguous():
@@ -217,6 +252,12 @@ class OneBitAdam:
         if src.dtype != torch.float32 or not src.is_contiguous():
             raise ValueError("source must be a contiguous float32 tensor")
         ob_adam_set_state(self.h, field, offset, src.numel(), src.data_ptr())
+
+    def checkpoint(self, device="cpu"):
+        """(copy of the workspace bytes, counters): the whole optimizer state."""
+        counters = ob_adam_get_counters(self.h)
+        self.stream.synchronize()
+        return self.workspace.to(device, copy=True), counters
 
     def params_view(self):
         """fp32[d] tensor aliasing the library's parameters x (no copy)."""

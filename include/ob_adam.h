@@ -152,6 +152,28 @@ ob_status ob_adam_set_state(ob_adam_t h, int32_t field, int64_t offset, int64_t 
  * read and write x between steps, ordered on the handle's stream. */
 ob_status ob_adam_params(ob_adam_t h, float** x_device);
 
+/* Checkpoint / resume.  The whole optimizer state is the workspace bytes
+ * plus these three counters (the segment partials inside the workspace are
+ * scratch and may be anything).  To checkpoint: let the stream pass the last
+ * step, copy ws_bytes of the workspace and read the counters.  To resume:
+ * put the copy into a workspace (same config, same size, 256-byte aligned)
+ * and attach it; later steps are bit-identical to an uninterrupted run. */
+typedef struct {
+  int64_t steps;            /* warm-up + compressed steps taken */
+  int64_t compressed_steps; /* compressed steps taken */
+  int64_t warmup_steps;     /* warm-up steps taken */
+} ob_adam_counters;
+
+/* OB_ERR_PHASE while a worker-at-a-time step is open. */
+ob_status ob_adam_get_counters(ob_adam_t h, ob_adam_counters* out);
+
+/* Like ob_adam_init, but adopts a workspace that already holds a state
+ * (nothing is cleared or enqueued).  OB_ERR_ARG for counters that no run
+ * can produce (negative, steps != warm-up + compressed, compressed steps
+ * without a warm-up step). */
+ob_status ob_adam_attach(const ob_adam_config* cfg, void* workspace, uint64_t ws_bytes,
+                         const ob_adam_counters* counters, void* stream, ob_adam_t* out);
+
 /* Steps taken so far (warm-up and compressed) and compressed steps taken. */
 ob_status ob_adam_step_count(ob_adam_t h, int64_t* steps, int64_t* compressed_steps);
 

@@ -79,3 +79,15 @@ def test_front_end_flat_layout(ob):
     assert d == 4 * 64 * 19  # 4736 rounded up to a multiple of 256
     offs, d = flat_layout([1], 8)
     assert offs == [0] and d == 512
+
+
+def test_attach_rejects_impossible_counters_without_gpu(ob):
+    cfg = ob.make_config(1 << 12, 4)
+    need = ob.ob_adam_workspace_bytes(cfg)
+    for counters in ((-1, 0, 0), (3, 1, 1), (2, 2, 0), (1, 0, 2)):
+        with pytest.raises(ob.ObAdamError) as e:
+            ob.ob_adam_attach(cfg, 256, need, counters, None)
+        assert e.value.status == ob.OB_ERR_ARG
+    with pytest.raises(ob.ObAdamError) as e:
+        ob.ob_adam_attach(cfg, 256, need - 1, (3, 1, 2), None)
+    assert e.value.status == ob.OB_ERR_WORKSPACE

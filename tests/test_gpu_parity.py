@@ -189,3 +189,29 @@ def test_slices_match_whole_fields():
         assert ulp_diff(part, whole[1000:4000]) == 0
     bits = gpu_np(opt, ob.OB_BITS_WORKER, 2, 5, 7)
     np.testing.assert_array_equal(bits, orc.get(oracle.BITS_WORKER, 2)[5:12])
+
+
+def test_checkpoint_resume_is_bit_identical():
+    """Save the state mid-run (workspace bytes + counters), keep going, then
+    resume the copy in a fresh handle: the continuation is bit-identical."""
+    import torch
+    d, n = 4 * 3392, 4
+    a = ob.OneBitAdam(d, n)
+    grads = [[to_device_grad(g) for g in host_grads(d, n, t, sigma=1e-2)] for t in range(7)]
+    for t in range(4):
+        (a.warmup_step if t < 2 else a.compressed_step)(grads[t], 1e-3)
+    ckpt = a.checkpoint()
+    assert ckpt[1] == (4, 2, 2)
+    for t in range(4, 7):
+        a.compressed_step(grads[t], 1e-3)
+    b = ob.OneBitAdam(d, n, checkpoint=ckpt)
+    assert b.steps == (4, 2)
+    for t in range(4, 7):
+        b.compressed_step(grads[t], 1e-3)
+    torch.cuda.synchronize()
+    assert a.steps == b.steps == (7, 5)
+    for f in (ob.OB_X, ob.OB_M, ob.OB_V, ob.OB_E_SERVER, ob.OB_BITS_SERVER, ob.OB_SCALE_SERVER):
+        np.testing.assert_array_equal(gpu_np(a, f), gpu_np(b, f))
+    for w in range(n):
+        for f in (ob.OB_E_WORKER, ob.OB_BITS_WORKER, ob.OB_SCALE_WORKER):
+            np.testing.assert_array_equal(gpu_np(a, f, w), gpu_np(b, f, w))
