@@ -51,7 +51,7 @@ def alg_bytes(w):
     }
 
 
-def survey_b_alg(w):
+def fp32_momentum_step_bytes(w):
     """Bytes per step with the momentum kept in fp32 (read and written each
     step) and the server-bit read counted per worker: d*[n*(gb+8.25)+28.125]."""
     gb = 2 if w.bf16 else 4
@@ -311,9 +311,9 @@ def main():
                      "alg_bytes_per_launch": wk["alg_bytes"]},
         "step": {"alg_bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                  "frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "fp32_momentum_bytes": survey_b_alg(w),
+                 "fp32_momentum_bytes": fp32_momentum_step_bytes(w),
                  "fp32_momentum_frac_of_peak": round(
-                     survey_b_alg(w) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     fp32_momentum_step_bytes(w) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "wall_s": round(wall, 4),
                  "ms_per_step_with_kernel_events": round(ms_step_timed, 4),
                  "timing_launches_dropped": dropped},
