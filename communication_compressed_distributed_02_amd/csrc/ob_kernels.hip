@@ -126,6 +126,65 @@ __device__ __forceinline__ float pairwise_sum_any(float* v, int n) {
 
 // ----------------------------------------------------------------- warm-up --
 // Full-precision Adam with bias correction on the pairwise worker average.
+__device__ __forceinline__ void adam_element(float gbar, float& m, float& v, float& x,
+                                             float beta1, float ob1, float beta2, float ob2,
+                                             float bc1, float bc2, float lr, float eps) {
+  m = (beta1 * m) + (ob1 * gbar);
+  v = (beta2 * v) + (ob2 * (gbar * gbar));
+  const float mh = m / bc1;
+  const float vh = v / bc2;
+  x = x - lr * (mh / (sqrtf(vh) + eps));
+}
+
+// NW a power of two: a wave owns R consecutive rows of 64 at a time (R = 4,
+// 2, 1 as NW grows, so the NW*R gradient registers stay bounded), issues all
+// loads of those rows first and streams them non-temporally.
+template <typename GT, int NW>
+__global__ void __launch_bounds__(kBlock)
+    warmup_rows_kernel(GradPtrs g, int64_t words, float* __restrict__ m, float* __restrict__ v,
+                       float* __restrict__ x, float beta1, float ob1, float beta2, float ob2,
+                       float bc1, float bc2, float lr, float eps) {
+  constexpr int R = NW <= 8 ? 4 : (NW <= 16 ? 2 : 1);
+  const int lane = threadIdx.x & 63;
+  const int64_t ngroups = words / R;  // full groups; a tail of rows is handled below
+  const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
+  const int64_t first = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
+  for (int64_t gi = first; gi < ngroups; gi += nwave) {
+    const int64_t k0 = gi * R * 64 + lane;
+    float gv[R][NW], mv[R], vv[R], xv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) gv[r][w] = grad_value((const GT*)g.p[w], k0 + 64 * r);
+      mv[r] = ld_stream(m + k0 + 64 * r);
+      vv[r] = ld_stream(v + k0 + 64 * r);
+      xv[r] = ld_stream(x + k0 + 64 * r);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float gbar = pairwise_sum<NW>(gv[r]) / (float)NW;
+      adam_element(gbar, mv[r], vv[r], xv[r], beta1, ob1, beta2, ob2, bc1, bc2, lr, eps);
+      st_stream(m + k0 + 64 * r, mv[r]);
+      st_stream(v + k0 + 64 * r, vv[r]);
+      st_stream(x + k0 + 64 * r, xv[r]);
+    }
+  }
+  // rows past the last full group: one row per wave
+  for (int64_t row = ngroups * R + first; row < words; row += nwave) {
+    const int64_t k = row * 64 + lane;
+    float vals[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) vals[w] = grad_value((const GT*)g.p[w], k);
+    const float gbar = pairwise_sum<NW>(vals) / (float)NW;
+    float mk = m[k], vk = v[k], xk = x[k];
+    adam_element(gbar, mk, vk, xk, beta1, ob1, beta2, ob2, bc1, bc2, lr, eps);
+    m[k] = mk;
+    v[k] = vk;
+    x[k] = xk;
+  }
+}
+
+// Any n <= 64 (run-time count, pairwise with odd tails): one element per thread.
 template <typename GT, int NW>
 __global__ void __launch_bounds__(kBlock)
     warmup_kernel(GradPtrs g, int n, int64_t d, float* __restrict__ m, float* __restrict__ v,
@@ -144,13 +203,11 @@ __global__ void __launch_bounds__(kBlock)
       sum = pairwise_sum_any(vals, n);
     }
     const float gbar = sum / (float)(NW > 0 ? NW : n);
-    const float mk = (beta1 * m[k]) + (ob1 * gbar);
-    const float vk = (beta2 * v[k]) + (ob2 * (gbar * gbar));
+    float mk = m[k], vk = v[k], xk = x[k];
+    adam_element(gbar, mk, vk, xk, beta1, ob1, beta2, ob2, bc1, bc2, lr, eps);
     m[k] = mk;
     v[k] = vk;
-    const float mh = mk / bc1;
-    const float vh = vk / bc2;
-    x[k] = x[k] - lr * (mh / (sqrtf(vh) + eps));
+    x[k] = xk;
   }
 }
 
@@ -681,8 +738,15 @@ hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1,
                          hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const float ob1 = 1.0f - s.beta1, ob2 = 1.0f - s.beta2;
   const dim3 grid(grid_for(s.d, kBlock, 8192));
-#define OB_WARM(GT, NW)                                                                     \
-  return launch(warmup_kernel<GT, NW>, grid, dim3(kBlock), stream, t0, t1, g, s.n, s.d, s.m, \
+  // one wave per group of rows: ceil(words / R) waves, R from the worker count
+  const int64_t R = s.n <= 8 ? 4 : (s.n <= 16 ? 2 : 1);
+  const dim3 rows_grid(grid_for((s.words + R - 1) / R, kWavesPerBlock, 1 << 20));
+#define OB_WARM(GT, NW)                                                                         \
+  if (NW > 0)                                                                                   \
+    return launch(warmup_rows_kernel<GT, (NW > 0 ? NW : 1)>, rows_grid, dim3(kBlock), stream,   \
+                  t0, t1, g, s.words, s.m, s.v, s.x, s.beta1, ob1, s.beta2, ob2, bc1, bc2, lr,  \
+                  s.eps);                                                                       \
+  return launch(warmup_kernel<GT, NW>, grid, dim3(kBlock), stream, t0, t1, g, s.n, s.d, s.m,     \
                 s.v, s.x, s.beta1, ob1, s.beta2, ob2, bc1, bc2, lr, s.eps)
 #define OB_WARM_N(GT)                \
   switch (s.n) {                     \
