@@ -26,6 +26,13 @@
 //  - Sign words are read with scalar (uniform) loads and decoded with an
 //    inverse ballot: bit `lane` of a uniform 64-bit word selects +s or -s in
 //    one v_cndmask.
+//  - The grid is non-persistent (one wave per segment, grid.y = worker x
+//    chunk): persistent grids and several segments per wave measured slower.
+//  - The server folds the workers' +-s in worker order into per-row stacks
+//    that reproduce the pairwise-by-levels sum exactly; from 32 workers on it
+//    works 8 rows at a time over batches of 4 workers to bound registers.
+//  - Per-chunk scales come from two small kernels: aligned groups of 512
+//    segment partials folded in parallel, then one block per chunk.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -36,37 +43,17 @@
 namespace ob {
 namespace {
 
-#ifndef OB_BLOCK
-#define OB_BLOCK 256
-#endif
-constexpr int kBlock = OB_BLOCK;
+constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / 64;
-
-// Launch-shape knobs (blocks along a chunk's segments per grid row).
-#ifndef OB_WORKER_BLOCKS_PER_ROW
-#define OB_WORKER_BLOCKS_PER_ROW (1 << 20)
-#endif
-#ifndef OB_SERVER_BLOCKS_PER_ROW
-#define OB_SERVER_BLOCKS_PER_ROW (1 << 20)
-#endif
-#ifndef OB_UPDATE_BLOCKS
-#define OB_UPDATE_BLOCKS (1 << 20)
-#endif
+constexpr int64_t kMaxBlocksPerRow = int64_t(1) << 20;
 
 // Streamed (read-once / write-once per step) accesses are non-temporal: the
 // step's working set is many times the caches, so nothing streamed is reused
-// before eviction.
-#ifndef OB_NO_NT_STREAM
+// before eviction (worker pass 1.94 -> 1.48 ms on 110M x 8 workers).
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
 template <typename T>
 __device__ __forceinline__ void st_stream(T* p, T v) { __builtin_nontemporal_store(v, p); }
-#else
-template <typename T>
-__device__ __forceinline__ T ld_stream(const T* p) { return *p; }
-template <typename T>
-__device__ __forceinline__ void st_stream(T* p, T v) { *p = v; }
-#endif
 
 // Index of this wavefront in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_in_block() {
@@ -230,58 +217,6 @@ __device__ __forceinline__ void worker_row(const GT* __restrict__ g, float* __re
   acc = add_square(acc, cv);
 }
 
-// One full segment: all 32 loads are issued before any use.
-template <typename GT, bool MBITS>
-struct SegIn {
-  float g[kSegRows];
-  float c[kSegRows];
-  float m[kSegRows];
-};
-
-template <typename GT, bool MBITS>
-__device__ __forceinline__ void load_segment(SegIn<GT, MBITS>& in, const GT* __restrict__ g,
-                                             const float* __restrict__ c,
-                                             const float* __restrict__ m,
-                                             const uint64_t* __restrict__ sbits, float ms,
-                                             int64_t base, int lane) {
-#pragma unroll
-  for (int r = 0; r < kSegRows; ++r) {
-    in.g[r] = grad_value(g, base + 64 * r + lane);
-    in.c[r] = ld_stream(c + base + 64 * r + lane);
-  }
-#pragma unroll
-  for (int r = 0; r < kSegRows; ++r)
-    in.m[r] = MBITS ? signed_scale(sbits[(base >> 6) + r], ms) : m[base + 64 * r + lane];
-}
-
-template <typename GT, bool MBITS>
-__device__ __forceinline__ void compute_segment(const SegIn<GT, MBITS>& in, float* __restrict__ c,
-                                                uint64_t* __restrict__ bits,
-                                                double* __restrict__ part, int64_t base,
-                                                int lane, float sp, float beta1, float ob1) {
-  double acc = 0.0;
-  uint64_t mine = 0;
-#pragma unroll
-  for (int r = 0; r < kSegRows; ++r) {
-    const float e = in.c[r] - (in.c[r] >= 0.0f ? sp : -sp);
-    const float cv = ((beta1 * in.m[r]) + (ob1 * in.g[r])) + e;
-    st_stream(c + base + 64 * r + lane, cv);
-    const uint64_t word = __ballot(cv >= 0.0f);
-    mine = lane == r ? word : mine;
-    acc = add_square(acc, cv);
-  }
-  acc = butterfly(acc);
-  if (lane < kSegRows) bits[(base >> 6) + lane] = mine;
-  if (lane == 0) *part = acc;
-}
-
-#ifndef OB_WORKER_SEGS_PER_WAVE
-#define OB_WORKER_SEGS_PER_WAVE 1
-#endif
-#ifndef OB_WORKER_ROWWISE
-#define OB_WORKER_ROWWISE 1
-#endif
-
 template <typename GT, bool MBITS>
 __global__ void __launch_bounds__(kBlock)
     worker_kernel(GradPtrs g, int w0, int64_t d, int64_t L, int n, int64_t nseg, int64_t words,
@@ -289,7 +224,6 @@ __global__ void __launch_bounds__(kBlock)
                   const float* __restrict__ sscale, float* __restrict__ cbuf,
                   const float* __restrict__ wscale, uint64_t* __restrict__ wbits,
                   double* __restrict__ wpart, float beta1, float ob1) {
-  constexpr int SPW = OB_WORKER_SEGS_PER_WAVE;
   const int lane = threadIdx.x & 63;
   const int wi = (int)blockIdx.y / n;  // worker within this launch
   const int j = (int)blockIdx.y - wi * n;
@@ -300,54 +234,27 @@ __global__ void __launch_bounds__(kBlock)
   double* __restrict__ part = wpart + ((int64_t)w * n + j) * nseg;
   const float sp = wscale[w * n + j];  // this worker's scale of chunk j, previous step
   const float ms = MBITS ? sscale[j] : 0.0f;
-  const int64_t full = L / kSegElems;  // segments with all 16 rows
   const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t s0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave_in_block()) * SPW; s0 < nseg;
-       s0 += nwave * SPW) {
-#if OB_WORKER_ROWWISE
-    if (s0 + SPW <= full) {
+  for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); s < nseg;
+       s += nwave) {
+    const int64_t q0 = s * kSegElems;
+    const int64_t left = (L - q0) >> 6;
+    const int rows = left < kSegRows ? (int)left : kSegRows;
+    const int64_t base = (int64_t)j * L + q0;  // global index of the segment's first element
+    const int64_t wbase = base >> 6;
+    double acc = 0.0;
+    uint64_t mine = 0;
+    if (rows == kSegRows) {
+      // fully unrolled: the compiler issues all 32 loads of the segment first
 #pragma unroll
-      for (int q = 0; q < SPW; ++q) {
-        const int64_t base = (int64_t)j * L + (s0 + q) * kSegElems;
-        const int64_t wbase = base >> 6;
-        double acc = 0.0;
-        uint64_t mine = 0;
-#pragma unroll
-        for (int r = 0; r < kSegRows; ++r) {
-          uint64_t word;
-          const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
-          worker_row<GT, MBITS>(gp, c, m, mword, ms, base + 64 * r + lane, sp, beta1, ob1, acc,
-                                word);
-          mine = lane == r ? word : mine;
-        }
-        acc = butterfly(acc);
-        if (lane < kSegRows) bits[wbase + lane] = mine;
-        if (lane == 0) part[s0 + q] = acc;
+      for (int r = 0; r < kSegRows; ++r) {
+        uint64_t word;
+        const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
+        worker_row<GT, MBITS>(gp, c, m, mword, ms, base + 64 * r + lane, sp, beta1, ob1, acc,
+                              word);
+        mine = lane == r ? word : mine;
       }
-      continue;
-    }
-#else
-    if (s0 + SPW <= full) {
-      SegIn<GT, MBITS> in[SPW];
-#pragma unroll
-      for (int q = 0; q < SPW; ++q)
-        load_segment<GT, MBITS>(in[q], gp, c, m, sbits, ms, (int64_t)j * L + (s0 + q) * kSegElems,
-                                lane);
-#pragma unroll
-      for (int q = 0; q < SPW; ++q)
-        compute_segment<GT, MBITS>(in[q], c, bits, part + s0 + q,
-                                   (int64_t)j * L + (s0 + q) * kSegElems, lane, sp, beta1, ob1);
-      continue;
-    }
-#endif
-    for (int64_t s = s0; s < s0 + SPW && s < nseg; ++s) {
-      const int64_t q0 = s * kSegElems;
-      const int64_t left = (L - q0) >> 6;
-      const int rows = left < kSegRows ? (int)left : kSegRows;
-      const int64_t base = (int64_t)j * L + q0;  // global index of the segment's first element
-      const int64_t wbase = base >> 6;
-      double acc = 0.0;
-      uint64_t mine = 0;
+    } else {
       for (int r = 0; r < rows; ++r) {
         uint64_t word;
         const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
@@ -355,10 +262,10 @@ __global__ void __launch_bounds__(kBlock)
                               word);
         mine = lane == r ? word : mine;
       }
-      acc = butterfly(acc);
-      if (lane < rows) bits[wbase + lane] = mine;
-      if (lane == 0) part[s] = acc;
     }
+    acc = butterfly(acc);
+    if (lane < rows) bits[wbase + lane] = mine;
+    if (lane == 0) part[s] = acc;
   }
 }
 
@@ -740,7 +647,7 @@ hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1,
   const dim3 grid(grid_for(s.d, kBlock, 8192));
   // one wave per group of rows: ceil(words / R) waves, R from the worker count
   const int64_t R = s.n <= 8 ? 4 : (s.n <= 16 ? 2 : 1);
-  const dim3 rows_grid(grid_for((s.words + R - 1) / R, kWavesPerBlock, 1 << 20));
+  const dim3 rows_grid(grid_for((s.words + R - 1) / R, kWavesPerBlock, kMaxBlocksPerRow));
 #define OB_WARM(GT, NW)                                                                         \
   if (NW > 0)                                                                                   \
     return launch(warmup_rows_kernel<GT, (NW > 0 ? NW : 1)>, rows_grid, dim3(kBlock), stream,   \
@@ -771,8 +678,7 @@ hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1,
 hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw, bool m_bits,
                               hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const float ob1 = 1.0f - s.beta1;
-  const dim3 grid(grid_for(s.nseg, kWavesPerBlock * OB_WORKER_SEGS_PER_WAVE, OB_WORKER_BLOCKS_PER_ROW),
-                  (unsigned)(nw * s.n));
+  const dim3 grid(grid_for(s.nseg, kWavesPerBlock, kMaxBlocksPerRow), (unsigned)(nw * s.n));
 #define OB_WORK(GT, MB)                                                                        \
   return launch(worker_kernel<GT, MB>, grid, dim3(kBlock), stream, t0, t1, g, w0, s.d, s.L, s.n, \
                 s.nseg, s.words, (const float*)s.m, (const uint64_t*)s.sbits,                    \
@@ -820,7 +726,7 @@ hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t
 }
 
 hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  const dim3 grid(grid_for(s.nseg, kWavesPerBlock, OB_SERVER_BLOCKS_PER_ROW), (unsigned)s.n);
+  const dim3 grid(grid_for(s.nseg, kWavesPerBlock, kMaxBlocksPerRow), (unsigned)s.n);
 #define OB_SRV(NW)                                                                             \
   return launch(server_kernel<NW>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n, s.nseg,       \
                 s.words, (const uint64_t*)s.wbits, (const float*)s.wscale, s.u,                 \
@@ -845,7 +751,7 @@ hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t
 hipError_t launch_update(const State& s, float lr, hipStream_t stream, hipEvent_t t0,
                          hipEvent_t t1) {
   const int64_t groups = (s.words + kSegRows - 1) / kSegRows;
-  return launch(update_kernel, dim3(grid_for(groups, kWavesPerBlock, OB_UPDATE_BLOCKS)),
+  return launch(update_kernel, dim3(grid_for(groups, kWavesPerBlock, kMaxBlocksPerRow)),
                 dim3(kBlock), stream, t0, t1, s.words, s.L, (const uint64_t*)s.sbits,
                 (const float*)s.sscale, (const float*)s.v, s.x, lr, s.eps);
 }
