@@ -337,6 +337,44 @@ __global__ void __launch_bounds__(kBlock)
   if (t == 0) scale_out[row] = (float)(sqrt(S) / sqrt((double)L));
 }
 
+// Rows of at most kBlock * PER partials in one dispatch: thread t folds the
+// aligned run [PER*t, PER*t + PER) pairwise in registers (zeros past the
+// row), then the block folds the kBlock run sums pairwise -- the same tree as
+// the pairwise sum over the row padded to kBlock * PER.
+template <int PER>
+__global__ void __launch_bounds__(kBlock)
+    scale_direct_kernel(const double* __restrict__ part, int64_t nseg, int64_t L,
+                        float* __restrict__ scale_out) {
+  __shared__ double red[kBlock];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const double* __restrict__ p = part + row * nseg;
+  double v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t k = (int64_t)t * PER + i;
+    v[i] = k < nseg ? p[k] : 0.0;
+  }
+#pragma unroll
+  for (int h = PER / 2; h >= 1; h /= 2) {
+#pragma unroll
+    for (int i = 0; i < h; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  }
+  red[t] = v[0];
+  __syncthreads();
+  for (int h = kBlock / 2; h >= 1; h >>= 1) {
+    double val = 0.0;
+    if (t < h) val = red[2 * t] + red[2 * t + 1];
+    __syncthreads();
+    if (t < h) red[t] = val;
+    __syncthreads();
+  }
+  if (t == 0) {
+    const double S = red[0];
+    scale_out[row] = (float)(sqrt(S) / sqrt((double)L));
+  }
+}
+
 // ------------------------------------------------------------- server pass --
 // Server j: a = pairwise over workers of (bit ? s_wj : -s_wj) / n;
 // u = a + (u_prev - (u_prev >= 0 ? s_prev : -s_prev)); stores u, sign words,
@@ -701,6 +739,22 @@ hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw,
 static hipError_t launch_scales(const double* part, int64_t nseg, int64_t L, int rows,
                                 double* fold, float* scale_out, hipStream_t stream,
                                 hipEvent_t t0, hipEvent_t t1) {
+  int64_t width = 1;
+  while (width < nseg) width <<= 1;
+  if (width > kGroup && width <= (int64_t)kBlock * 64) {
+    const dim3 grid((unsigned)rows), block(kBlock);
+    if (width <= (int64_t)kBlock * 4)
+      return launch(scale_direct_kernel<4>, grid, block, stream, t0, t1, part, nseg, L, scale_out);
+    if (width <= (int64_t)kBlock * 8)
+      return launch(scale_direct_kernel<8>, grid, block, stream, t0, t1, part, nseg, L, scale_out);
+    if (width <= (int64_t)kBlock * 16)
+      return launch(scale_direct_kernel<16>, grid, block, stream, t0, t1, part, nseg, L,
+                    scale_out);
+    if (width <= (int64_t)kBlock * 32)
+      return launch(scale_direct_kernel<32>, grid, block, stream, t0, t1, part, nseg, L,
+                    scale_out);
+    return launch(scale_direct_kernel<64>, grid, block, stream, t0, t1, part, nseg, L, scale_out);
+  }
   const double* cur = part;
   int64_t cnt = nseg;
   double* out = fold;
