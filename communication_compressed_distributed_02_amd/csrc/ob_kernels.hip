@@ -741,7 +741,9 @@ static hipError_t launch_scales(const double* part, int64_t nseg, int64_t L, int
                                 hipEvent_t t0, hipEvent_t t1) {
   int64_t width = 1;
   while (width < nseg) width <<= 1;
-  if (width > kGroup && width <= (int64_t)kBlock * 64) {
+  // one dispatch for moderate rows; with thousands of rows (n*n worker rows at
+  // large n) the parallel group fold below keeps more waves busy
+  if (width > kGroup && width <= (int64_t)kBlock * 64 && rows <= 512) {
     const dim3 grid((unsigned)rows), block(kBlock);
     if (width <= (int64_t)kBlock * 4)
       return launch(scale_direct_kernel<4>, grid, block, stream, t0, t1, part, nseg, L, scale_out);
