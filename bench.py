@@ -106,7 +106,7 @@ def cpu_baseline(w, steps=1):
 
 
 PROBE_LIB = os.path.join(ROOT, "communication_compressed_distributed_02_amd", "libob_probe.so")
-PROBE_KINDS = {"mix": 0, "copy": 1, "read": 2, "write": 3}
+PROBE_KINDS = {"mix": 0, "copy": 1, "read": 2, "write": 3, "mix32": 4}
 
 
 def probe_lib():
@@ -147,18 +147,20 @@ def copy_calibration(mib):
                       "read": "reads 4n", "write": "writes 4n", "dispatches_each": 3}), flush=True)
 
 
-def stream_ceilings(n, reps=5):
+def stream_ceilings(n, bf16=True, reps=5):
     """GB/s of the probes over n elements on this device: the worker pass's
-    access mix (6 B read + 4 B written per element), copy, read-only and
-    write-only, with the step's own wave-row mapping and non-temporal hints."""
+    access mix (bf16 gradients: 6 B read + 4 B written per element; fp32:
+    8 + 4), copy, read-only and write-only, with the step's own wave-row
+    mapping and non-temporal hints."""
     import torch
     lib = probe_lib()
     n -= n % 4096
-    g = torch.zeros(n, dtype=torch.int16, device="cuda:0")
+    g = torch.zeros(n, dtype=torch.int16 if bf16 else torch.float32, device="cuda:0")
     c = torch.zeros(n, dtype=torch.float32, device="cuda:0")
     c2 = torch.zeros(n, dtype=torch.float32, device="cuda:0")
     out = {}
-    for kind, a, b, nbytes in (("mix", g, c, 10 * n), ("copy", c, c2, 8 * n),
+    mix = ("mix", g, c, 10 * n) if bf16 else ("mix32", g, c, 12 * n)
+    for kind, a, b, nbytes in (mix, ("copy", c, c2, 8 * n),
                                ("read", c, c2, 4 * n), ("write", None, c2, 4 * n)):
         for _ in range(2):
             run_probe(lib, kind, a, b, n)
@@ -169,7 +171,8 @@ def stream_ceilings(n, reps=5):
             run_probe(lib, kind, a, b, n)
         e1.record()
         torch.cuda.synchronize()
-        out[kind + "_GB_s"] = round(nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        out[("mix" if kind == "mix32" else kind) + "_GB_s"] = round(
+            nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     del g, c, c2
     torch.cuda.empty_cache()
     return out
@@ -321,9 +324,10 @@ def main():
     }
     del grads, ring_grads, opt
     torch.cuda.empty_cache()
-    ceil = stream_ceilings(w.n * w.d if not w.staged else w.d)
+    ceil = stream_ceilings(min(w.n * w.d if not w.staged else w.d, 1 << 31), w.bf16)
     ceil["note"] = ("probe kernels with the worker pass's mapping over as many elements as one "
-                    "launch of it; mix = its 6 B read + 4 B written per element")
+                    "launch of it (at most 2^31); mix = its %d B read + 4 B written per element"
+                    % (6 if w.bf16 else 8))
     ceil["worker_frac_of_mix"] = round(wk["GB_s"] / ceil["mix_GB_s"], 4)
     result["ceilings"] = ceil
     if not a.no_cpu_baseline:

@@ -423,20 +423,31 @@ __device__ __forceinline__ void server_average_segment(const uint64_t* __restric
   for (int r = 0; r < kSegRows; ++r) avg[r] = stack[LEVELS - 1][r] / (float)NW;
 }
 
-// Many workers (NW >= 32, a power of two): R rows at a time, workers in
-// batches of 4 (one burst of four 64-byte scalar loads per batch, the 4-worker
-// subtree formed in registers), batches folded into per-row stacks in batch
-// order -- again exactly the pairwise-by-levels sum -- with the stack levels as
+// Many workers (NW >= 16, a power of two): R rows at a time, workers in
+// batches of B (one burst of B scalar loads per batch, the B-worker subtree
+// formed in registers), batches folded into per-row stacks in batch order --
+// again exactly the pairwise-by-levels sum -- with the stack levels as
 // compile-time indices under a uniform run-time batch loop, which keeps the
-// register footprint (and so the occupancy) independent of NW.
-template <int NW, int R>
+// register footprint (and so the occupancy) from growing with NW.
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// Batch shape by worker count (measured): 16 workers -> batches of 2 over a
+// whole segment (server pass 1.09 -> 0.92 ms on 334M x 16); 32+ workers ->
+// batches of 4 over 8 rows (5.26 -> 2.15 ms on 340M x 64).
+template <int NW>
+struct ServerBatch {
+  static constexpr int workers = NW == 16 ? 2 : 4;
+  static constexpr int rows = NW == 16 ? kSegRows : 8;
+};
+
+template <int NW, int R, int B = ServerBatch<NW>::workers>
 __device__ __forceinline__ void server_average_rows(const uint64_t* __restrict__ wbits,
                                                     int64_t words, int64_t wbase,
                                                     const float* sws, float* avg) {
-  constexpr int B = 4;
   constexpr int NB = NW / B;
-  constexpr int LB = NB == 4 ? 3 : NB == 8 ? 4 : NB == 16 ? 5 : 6;  // log2(NB) + 1
-  static_assert(NW >= 16 && NW <= 128 && (NW & (NW - 1)) == 0, "power of two, 16..128");
+  constexpr int LB = ilog2(NB) + 1;
+  static_assert(NW >= 8 && NW <= 128 && (NW & (NW - 1)) == 0, "power of two, 8..128");
+  static_assert(B == 2 || B == 4 || B == 8, "batch of 2, 4 or 8 workers");
   // (used from NW = 32 on: at 16 workers the fully unrolled segment path is faster)
   float stack[LB][R];
 #pragma unroll 1
@@ -454,11 +465,10 @@ __device__ __forceinline__ void server_average_rows(const uint64_t* __restrict__
     float v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float a0 = signed_scale(wd[0][r], s[0]);
-      const float a1 = signed_scale(wd[1][r], s[1]);
-      const float a2 = signed_scale(wd[2][r], s[2]);
-      const float a3 = signed_scale(wd[3][r], s[3]);
-      v[r] = (a0 + a1) + (a2 + a3);
+      float a[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) a[q] = signed_scale(wd[q][r], s[q]);
+      v[r] = pairwise_sum<B>(a);  // the batch is an aligned subtree of the worker tree
     }
     int x = b;
     bool carry = true;
@@ -491,14 +501,15 @@ __global__ void __launch_bounds__(kBlock)
   const int j = blockIdx.y;
   // per-chunk worker scales in registers for the small-NW paths; the
   // many-worker path reads them per batch instead
-  constexpr int WS = NW >= 32 ? 1 : (NW > 0 ? NW : kMaxWorkersPerLaunch);
+  constexpr bool BATCHED = NW >= 16;
+  constexpr int WS = BATCHED ? 1 : (NW > 0 ? NW : kMaxWorkersPerLaunch);
   float ws[WS];
   const int nw = NW > 0 ? NW : n;
 #pragma unroll
   for (int w = 0; w < WS; ++w)
     if (w < nw) ws[w] = wscale[w * n + j];
-  __shared__ float sws[NW >= 32 ? NW : 1];
-  if constexpr (NW >= 32) {
+  __shared__ float sws[BATCHED ? NW : 1];
+  if constexpr (BATCHED) {
     if ((int)threadIdx.x < NW) sws[threadIdx.x] = wscale[threadIdx.x * n + j];
     __syncthreads();
   }
@@ -519,10 +530,11 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
         for (int r = 0; r < kSegRows; ++r) up[r] = ld_stream(u + base + 64 * r + lane);
         float avg[kSegRows];
-        if constexpr (NW >= 32) {
-          server_average_rows<NW, kSegRows / 2>(wbits, words, wbase, sws, avg);
-          server_average_rows<NW, kSegRows / 2>(wbits, words, wbase + kSegRows / 2, sws,
-                                                avg + kSegRows / 2);
+        if constexpr (BATCHED) {
+          constexpr int RB = ServerBatch<NW>::rows;
+#pragma unroll
+          for (int h = 0; h < kSegRows / RB; ++h)
+            server_average_rows<NW, RB>(wbits, words, wbase + h * RB, sws, avg + h * RB);
         } else {
           server_average_segment<NW>(wbits, words, wbase, ws, avg);
         }
@@ -546,7 +558,7 @@ __global__ void __launch_bounds__(kBlock)
       const float up = u[k];
       const float e = up - (up >= 0.0f ? sp : -sp);
       float a;
-      if constexpr (NW >= 32) {
+      if constexpr (BATCHED) {
         server_average_rows<NW, 1>(wbits, words, wbase + r, sws, &a);
       } else {
         a = worker_average<NW>(wbits, words, wbase + r, ws, n);

@@ -37,6 +37,22 @@ __global__ void __launch_bounds__(kBlock) mix_kernel(const uint16_t* __restrict_
   for (int r = 0; r < 16; ++r) st_nt(c + base + 64 * r + lane, cv[r] * 0.5f + gv[r]);
 }
 
+// 8 bytes read + 4 written per element: the worker pass's mix with fp32
+// gradients (fp32 in, fp32 in/out).
+__global__ void __launch_bounds__(kBlock) mix32_kernel(const float* __restrict__ g,
+                                                       float* __restrict__ c) {
+  const int lane = threadIdx.x & 63;
+  const int64_t base = wave_base();
+  float gv[16], cv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    gv[r] = ld_nt(g + base + 64 * r + lane);
+    cv[r] = ld_nt(c + base + 64 * r + lane);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) st_nt(c + base + 64 * r + lane, cv[r] * 0.5f + gv[r]);
+}
+
 // 4 bytes read + 4 written per element: a plain copy.
 __global__ void __launch_bounds__(kBlock) copy_kernel(const float* __restrict__ a,
                                                       float* __restrict__ b) {
@@ -72,11 +88,12 @@ __global__ void __launch_bounds__(kBlock) write_kernel(float* __restrict__ b) {
 }  // namespace
 
 // kind: 0 = mix (a: bf16 elements, b: fp32 elements), 1 = copy a -> b (fp32),
-// 2 = read a (fp32; b receives at most one float), 3 = write b (fp32).
+// 2 = read a (fp32; b receives at most one float), 3 = write b (fp32),
+// 4 = mix with fp32 a.
 // n: elements, a positive multiple of 4096 (whole blocks); returns 0 on
 // success, 1 for bad arguments, 2 for a launch error.
 extern "C" int ob_probe_run(int kind, const void* a, void* b, int64_t n, void* stream) {
-  if (n <= 0 || n % 4096 != 0 || kind < 0 || kind > 3) return 1;
+  if (n <= 0 || n % 4096 != 0 || kind < 0 || kind > 4) return 1;
   if ((kind != 3 && a == nullptr) || b == nullptr) return 1;
   const int64_t blocks = n / 4096;
   if (blocks > 0x7fffffff) return 1;
@@ -87,6 +104,7 @@ extern "C" int ob_probe_run(int kind, const void* a, void* b, int64_t n, void* s
     case 1: copy_kernel<<<grid, block, 0, s>>>((const float*)a, (float*)b); break;
     case 2: read_kernel<<<grid, block, 0, s>>>((const float*)a, (float*)b); break;
     case 3: write_kernel<<<grid, block, 0, s>>>((float*)b); break;
+    case 4: mix32_kernel<<<grid, block, 0, s>>>((const float*)a, (float*)b); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
