@@ -31,6 +31,8 @@ def _lib():
 CASES = [
     # (name, d, n, bf16, sigma, warm, comp)
     ("n1_one_segment", 1024, 1, False, 1e-2, 2, 3),
+    ("n1_minimum_d64", 64, 1, False, 1e-2, 1, 3),
+    ("n4_one_row_chunks", 4 * 64, 4, True, 1e-3, 2, 3),
     ("n3_ragged", 3 * 1472, 3, False, 1e-2, 2, 4),
     ("n4_ragged", 4 * 3392, 4, False, 1e-2, 2, 4),
     ("n5_generic", 5 * 2112, 5, False, 1e-2, 1, 3),
