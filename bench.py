@@ -236,7 +236,12 @@ def main():
     opt = ob.OneBitAdam(w.d, w.n, ob.OB_GRAD_BF16 if w.bf16 else ob.OB_GRAD_F32, w.beta1,
                         w.beta2, w.eps, device=dev)
     for t in range(w.warmup):
-        opt.warmup_step(grads[t], w.lr_at(t))
+        if w.staged:
+            for i in range(w.n):
+                opt.warmup_worker(i, grads[t][i])
+            opt.warmup_finish(w.lr_at(t))
+        else:
+            opt.warmup_step(grads[t], w.lr_at(t))
     for t in range(w.warmup, w.warmup + a.warmup):
         step(opt, t)
     torch.cuda.synchronize()

@@ -20,6 +20,8 @@ struct ob_adam_handle {
   int64_t warm;         // warm-up steps taken
   bool staged_open;     // a worker-at-a-time step has started
   uint64_t staged_mask; // workers already compressed in the open step
+  bool warm_open;       // a worker-at-a-time warm-up step has started
+  int warm_next;        // the next worker that step expects
   bool poisoned;
   // per-kernel timing (events recorded around each launch when enabled)
   std::vector<hipEvent_t> ev;          // 2 per timed launch
@@ -93,6 +95,19 @@ ob_status gather_grads(ob_adam_t h, const void* const* grads, int w0, int nw, ob
   }
   (void)h;
   return OB_OK;
+}
+
+bool any_open(ob_adam_t h) { return h->staged_open || h->warm_open; }
+
+// Bias corrections (float)(1 - b^t) with b^t formed by t fp64 multiplications.
+void bias_corrections(const ob::State& s, int64_t t, float* bc1, float* bc2) {
+  double p1 = 1.0, p2 = 1.0;
+  for (int64_t i = 0; i < t; ++i) {
+    p1 = p1 * (double)s.beta1;
+    p2 = p2 * (double)s.beta2;
+  }
+  *bc1 = (float)(1.0 - p1);
+  *bc2 = (float)(1.0 - p2);
 }
 
 // Worker scales, server pass, server scales, update; then count the step.
@@ -217,7 +232,7 @@ ob_status ob_adam_attach(const ob_adam_config* cfg, void* workspace, uint64_t ws
 
 ob_status ob_adam_get_counters(ob_adam_t h, ob_adam_counters* out) {
   if (h == nullptr || out == nullptr) return OB_ERR_ARG;
-  if (h->staged_open) return OB_ERR_PHASE;
+  if (any_open(h)) return OB_ERR_PHASE;
   out->steps = h->steps;
   out->compressed_steps = h->compressed;
   out->warmup_steps = h->warm;
@@ -227,18 +242,13 @@ ob_status ob_adam_get_counters(ob_adam_t h, ob_adam_counters* out) {
 ob_status ob_adam_warmup_step(ob_adam_t h, const void* const* grads, float lr) {
   ob_status st = usable(h);
   if (st != OB_OK) return st;
-  if (h->compressed > 0 || h->staged_open) return OB_ERR_PHASE;
+  if (h->compressed > 0 || any_open(h)) return OB_ERR_PHASE;
   ob::GradPtrs g{};
   st = gather_grads(h, grads, 0, h->st.n, &g);
   if (st != OB_OK) return st;
   const int64_t t = h->steps + 1;
-  double p1 = 1.0, p2 = 1.0;
-  for (int64_t i = 0; i < t; ++i) {
-    p1 = p1 * (double)h->st.beta1;
-    p2 = p2 * (double)h->st.beta2;
-  }
-  const float bc1 = (float)(1.0 - p1);
-  const float bc2 = (float)(1.0 - p2);
+  float bc1, bc2;
+  bias_corrections(h->st, t, &bc1, &bc2);
   st = fail(h, timed(h, OB_K_WARMUP, [&](hipEvent_t a, hipEvent_t b) {
               return ob::launch_warmup(h->st, g, lr, bc1, bc2, h->stream, a, b);
             }));
@@ -248,10 +258,43 @@ ob_status ob_adam_warmup_step(ob_adam_t h, const void* const* grads, float lr) {
   return OB_OK;
 }
 
+ob_status ob_adam_warmup_worker(ob_adam_t h, int32_t worker, const void* grad) {
+  ob_status st = usable(h);
+  if (st != OB_OK) return st;
+  if (worker < 0 || worker >= h->st.n || grad == nullptr) return OB_ERR_ARG;
+  if (h->compressed > 0 || h->staged_open) return OB_ERR_PHASE;
+  if (worker != (h->warm_open ? h->warm_next : 0)) return OB_ERR_PHASE;
+  st = fail(h, timed(h, OB_K_WARMUP, [&](hipEvent_t a, hipEvent_t b) {
+              return ob::launch_warmup_push(h->st, grad, worker, h->stream, a, b);
+            }));
+  if (st != OB_OK) return st;
+  h->warm_open = true;
+  h->warm_next = worker + 1;
+  return OB_OK;
+}
+
+ob_status ob_adam_warmup_finish(ob_adam_t h, float lr) {
+  ob_status st = usable(h);
+  if (st != OB_OK) return st;
+  if (!h->warm_open || h->warm_next != h->st.n) return OB_ERR_PHASE;
+  const int64_t t = h->steps + 1;
+  float bc1, bc2;
+  bias_corrections(h->st, t, &bc1, &bc2);
+  st = fail(h, timed(h, OB_K_WARMUP, [&](hipEvent_t a, hipEvent_t b) {
+              return ob::launch_warmup_finish(h->st, lr, bc1, bc2, h->stream, a, b);
+            }));
+  if (st != OB_OK) return st;
+  h->warm_open = false;
+  h->warm_next = 0;
+  h->steps = t;
+  h->warm += 1;
+  return OB_OK;
+}
+
 ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float lr) {
   ob_status st = usable(h);
   if (st != OB_OK) return st;
-  if (h->warm == 0 || h->staged_open) return OB_ERR_PHASE;
+  if (h->warm == 0 || any_open(h)) return OB_ERR_PHASE;
   ob::GradPtrs g{};
   st = gather_grads(h, grads, 0, h->st.n, &g);
   if (st != OB_OK) return st;
@@ -267,7 +310,7 @@ ob_status ob_adam_compress_worker(ob_adam_t h, int32_t worker, const void* grad)
   ob_status st = usable(h);
   if (st != OB_OK) return st;
   if (worker < 0 || worker >= h->st.n || grad == nullptr) return OB_ERR_ARG;
-  if (h->warm == 0) return OB_ERR_PHASE;
+  if (h->warm == 0 || h->warm_open) return OB_ERR_PHASE;
   const uint64_t bit = (uint64_t)1 << worker;
   if (h->staged_open && (h->staged_mask & bit)) return OB_ERR_PHASE;
   ob::GradPtrs g{};
@@ -305,6 +348,9 @@ ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t 
   // mid-way through a worker-at-a-time step the compressed workers' slabs
   // already belong to the new step while the scales still belong to the old
   if (h->staged_open && (field == OB_E_WORKER || field == OB_BITS_WORKER)) return OB_ERR_PHASE;
+  // mid-way through a worker-at-a-time warm-up step the compensated slabs
+  // hold that step's partial gradient sums
+  if (h->warm_open && field == OB_E_WORKER) return OB_ERR_PHASE;
   int64_t size;
   switch (field) {
     case OB_X: case OB_M: case OB_V: case OB_E_WORKER: case OB_E_SERVER: size = s.d; break;
@@ -355,7 +401,7 @@ ob_status ob_adam_set_state(ob_adam_t h, int32_t field, int64_t offset, int64_t 
   if (field == OB_X) {
     dst = s.x;
   } else if (field == OB_V) {
-    if (h->compressed > 0 || h->staged_open) return OB_ERR_PHASE;
+    if (h->compressed > 0 || any_open(h)) return OB_ERR_PHASE;
     dst = s.v;
   } else {
     return OB_ERR_ARG;

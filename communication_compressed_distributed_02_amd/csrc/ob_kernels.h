@@ -47,6 +47,14 @@ Layout layout_for(int64_t d, int n);
 // end of the last dispatch of the launcher (null = untimed).
 hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1, float bc2,
                          hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+// Worker-at-a-time warm-up: the binary-counter stack of partial gradient sums
+// lives in the compensated slabs (levels 0..warmup_stack_levels(n)-1 of d
+// floats each, at most n), which the finish clears again.
+int warmup_stack_levels(int n);
+hipError_t launch_warmup_push(const State& s, const void* grad, int worker, hipStream_t stream,
+                              hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_warmup_finish(const State& s, float lr, float bc1, float bc2,
+                                hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw, bool m_bits,
                               hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);

@@ -171,6 +171,53 @@ __global__ void __launch_bounds__(kBlock)
   }
 }
 
+// Worker-at-a-time warm-up.  The gradients are summed in the pairwise order
+// by a binary-counter stack of partial sums, level l at stack + l*d: worker w
+// merges the levels 0..merges-1 (merges = trailing one bits of w), each as
+// (stack level) + (carry), and leaves its carry at level `merges`.  After all n
+// workers the occupied levels are the set bits of n; folding them from the
+// lowest level up, each as (higher level) + (carry), is exactly the
+// pairwise-by-levels sum with odd tails passing up.
+template <typename GT>
+__global__ void __launch_bounds__(kBlock)
+    warmup_push_kernel(const GT* __restrict__ g, float* __restrict__ stack, int64_t d,
+                       int merges) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < d; k += stride) {
+    float v = grad_value(g, k);
+    for (int l = 0; l < merges; ++l) v = ld_stream(stack + (int64_t)l * d + k) + v;
+    st_stream(stack + (int64_t)merges * d + k, v);
+  }
+}
+
+// Fold the stack, average, one Adam step; then clear every stack level used
+// (levels 0..levels-1), so the slabs hold zeros again.
+__global__ void __launch_bounds__(kBlock)
+    warmup_finish_kernel(float* __restrict__ stack, int64_t d, int n, int levels,
+                         float* __restrict__ m, float* __restrict__ v, float* __restrict__ x,
+                         float beta1, float ob1, float beta2, float ob2, float bc1, float bc2,
+                         float lr, float eps) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < d; k += stride) {
+    float acc = 0.0f;
+    bool have = false;
+    for (int l = 0; l < levels; ++l) {
+      if ((n >> l) & 1) {
+        const float s = ld_stream(stack + (int64_t)l * d + k);
+        acc = have ? s + acc : s;
+        have = true;
+      }
+    }
+    const float gbar = acc / (float)n;
+    float mk = m[k], vk = v[k], xk = x[k];
+    adam_element(gbar, mk, vk, xk, beta1, ob1, beta2, ob2, bc1, bc2, lr, eps);
+    m[k] = mk;
+    v[k] = vk;
+    x[k] = xk;
+    for (int l = 0; l < levels; ++l) st_stream(stack + (int64_t)l * d + k, 0.0f);
+  }
+}
+
 // Any n <= 64 (run-time count, pairwise with odd tails): one element per thread.
 template <typename GT, int NW>
 __global__ void __launch_bounds__(kBlock)
@@ -723,6 +770,32 @@ hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1,
   }
 #undef OB_WARM_N
 #undef OB_WARM
+}
+
+int warmup_stack_levels(int n) {
+  int levels = 0;
+  while ((1 << levels) <= n) ++levels;  // floor(log2(n)) + 1
+  return levels;
+}
+
+hipError_t launch_warmup_push(const State& s, const void* grad, int worker, hipStream_t stream,
+                              hipEvent_t t0, hipEvent_t t1) {
+  int merges = 0;
+  while ((worker >> merges) & 1) ++merges;
+  const dim3 grid(grid_for(s.d, kBlock, 8192));
+  if (s.grad_bf16)
+    return launch(warmup_push_kernel<uint16_t>, grid, dim3(kBlock), stream, t0, t1,
+                  (const uint16_t*)grad, s.c, s.d, merges);
+  return launch(warmup_push_kernel<float>, grid, dim3(kBlock), stream, t0, t1,
+                (const float*)grad, s.c, s.d, merges);
+}
+
+hipError_t launch_warmup_finish(const State& s, float lr, float bc1, float bc2,
+                                hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const float ob1 = 1.0f - s.beta1, ob2 = 1.0f - s.beta2;
+  return launch(warmup_finish_kernel, dim3(grid_for(s.d, kBlock, 8192)), dim3(kBlock), stream, t0,
+                t1, s.c, s.d, s.n, warmup_stack_levels(s.n), s.m, s.v, s.x, s.beta1, ob1,
+                s.beta2, ob2, bc1, bc2, lr, s.eps);
 }
 
 hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw, bool m_bits,

@@ -20,6 +20,7 @@ OB_GRAD_F32, OB_GRAD_BF16 = 0, 1
  OB_SCALE_SERVER) = range(9)
 
 EXPORTED = ("ob_adam_workspace_bytes", "ob_adam_init", "ob_adam_warmup_step",
+            "ob_adam_warmup_worker", "ob_adam_warmup_finish",
             "ob_adam_compressed_step", "ob_adam_compress_worker", "ob_adam_compressed_finish",
             "ob_adam_get_state", "ob_adam_set_state", "ob_adam_params", "ob_adam_step_count",
             "ob_adam_get_counters", "ob_adam_attach", "ob_adam_set_timing",
@@ -55,6 +56,8 @@ def _load(path=LIB_PATH):
         "ob_adam_init": [cfgp, P, U64, P, P, ctypes.POINTER(P)],
         "ob_adam_warmup_step": [P, ctypes.POINTER(P), F],
         "ob_adam_compressed_step": [P, ctypes.POINTER(P), F],
+        "ob_adam_warmup_worker": [P, I32, P],
+        "ob_adam_warmup_finish": [P, F],
         "ob_adam_compress_worker": [P, I32, P],
         "ob_adam_compressed_finish": [P, F],
         "ob_adam_get_state": [P, I32, I32, I64, I64, P],
@@ -113,6 +116,14 @@ def _ptr_array(ptrs):
 
 def ob_adam_warmup_step(h, grad_ptrs, lr):
     _check(_lib.ob_adam_warmup_step(h, _ptr_array(grad_ptrs), lr), "ob_adam_warmup_step")
+
+
+def ob_adam_warmup_worker(h, worker, grad_ptr):
+    _check(_lib.ob_adam_warmup_worker(h, worker, grad_ptr), "ob_adam_warmup_worker")
+
+
+def ob_adam_warmup_finish(h, lr):
+    _check(_lib.ob_adam_warmup_finish(h, lr), "ob_adam_warmup_finish")
 
 
 def ob_adam_compressed_step(h, grad_ptrs, lr):
@@ -228,6 +239,12 @@ class OneBitAdam:
 
     def warmup_step(self, grads, lr):
         ob_adam_warmup_step(self.h, self._grad_ptrs(grads), lr)
+
+    def warmup_worker(self, worker, grad):
+        ob_adam_warmup_worker(self.h, worker, self._grad_ptrs([grad])[0])
+
+    def warmup_finish(self, lr):
+        ob_adam_warmup_finish(self.h, lr)
 
     def compressed_step(self, grads, lr):
         ob_adam_compressed_step(self.h, self._grad_ptrs(grads), lr)

@@ -115,6 +115,20 @@ ob_status ob_adam_init(const ob_adam_config* cfg, void* workspace, uint64_t ws_b
  * OB_ERR_PHASE after any compressed step. */
 ob_status ob_adam_warmup_step(ob_adam_t h, const void* const* grads, float lr);
 
+/* The same warm-up step with the gradients supplied one worker at a time
+ * (bounded memory: a caller can regenerate each worker's gradient into one
+ * buffer).  Call ob_adam_warmup_worker for workers 0, 1, ..., n-1 in that
+ * order (`grad` is d device elements of cfg.grad_dtype and may be reused
+ * once the call's work has passed on the stream), then ob_adam_warmup_finish.
+ * The partial sums are kept in the workspace (in the worker error slabs,
+ * which are zero throughout the warm-up and are cleared again by the finish)
+ * and grouped exactly as the pairwise-by-levels sum, so results are identical
+ * to ob_adam_warmup_step.  OB_ERR_PHASE for a worker out of order, for finish
+ * before all n workers, after any compressed step, and for the other step
+ * calls while such a step is open. */
+ob_status ob_adam_warmup_worker(ob_adam_t h, int32_t worker, const void* grad);
+ob_status ob_adam_warmup_finish(ob_adam_t h, float lr);
+
 /* One compression-phase step (the contract above), all n workers at once.
  * grads as for ob_adam_warmup_step.  OB_ERR_PHASE before any warm-up step or
  * while a staged step is open.  The variance is the one left by the last
@@ -136,8 +150,9 @@ ob_status ob_adam_compressed_finish(ob_adam_t h, float lr);
  * device memory `dst_device`.  Derived fields (errors, decompressed momentum)
  * are materialized by a kernel.  Enqueued on the handle's stream; the range
  * must lie inside the field (OB_ERR_ARG otherwise).  OB_E_WORKER and
- * OB_BITS_WORKER are refused (OB_ERR_PHASE) while a worker-at-a-time step is
- * open, as they would mix the old and the new step. */
+ * OB_BITS_WORKER are refused (OB_ERR_PHASE) while a worker-at-a-time
+ * compressed step is open, as they would mix the old and the new step, and
+ * OB_E_WORKER while a worker-at-a-time warm-up step is open. */
 ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t offset,
                             int64_t count, void* dst_device);
 
@@ -164,7 +179,7 @@ typedef struct {
   int64_t warmup_steps;     /* warm-up steps taken */
 } ob_adam_counters;
 
-/* OB_ERR_PHASE while a worker-at-a-time step is open. */
+/* OB_ERR_PHASE while a worker-at-a-time step (warm-up or compressed) is open. */
 ob_status ob_adam_get_counters(ob_adam_t h, ob_adam_counters* out);
 
 /* Like ob_adam_init, but adopts a workspace that already holds a state
@@ -179,7 +194,7 @@ ob_status ob_adam_step_count(ob_adam_t h, int64_t* steps, int64_t* compressed_st
 
 /* Kernels of a step, for ob_adam_kernel_times. */
 enum {
-  OB_K_WARMUP = 0,        /* warm-up Adam pass */
+  OB_K_WARMUP = 0,        /* warm-up Adam pass (staged: each worker's pass and the finish) */
   OB_K_WORKER = 1,        /* worker compress pass (all workers of one call) */
   OB_K_WORKER_SCALE = 2,  /* worker scale finalize */
   OB_K_SERVER = 3,        /* server average / re-compress pass */

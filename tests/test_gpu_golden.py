@@ -80,20 +80,27 @@ def test_full_size_against_stored_oracle(name):
         loc = torch.as_tensor(np.asarray(rec["idx"], dtype=np.int64) - j * L, device=dev)
         return opt.get(field, worker, j * L, L).index_select(0, loc).cpu().numpy()
 
-    full = torch.empty((n, w.d), dtype=gdt, device=dev)
+    # a staged workload regenerates each worker's gradient into one buffer, in
+    # the warm-up as in the compression phase
+    if w.staged:
+        one = torch.empty(w.d, dtype=gdt, device=dev)
+    else:
+        full = torch.empty((n, w.d), dtype=gdt, device=dev)
     for t in range(w.warmup):
-        for i in range(n):
-            fill(full[i], i, t)
-        opt.warmup_step(list(full.unbind(0)), w.lr_at(t))
+        if w.staged:
+            for i in range(n):
+                fill(one, i, t)
+                opt.warmup_worker(i, one)
+            opt.warmup_finish(w.lr_at(t))
+        else:
+            for i in range(n):
+                fill(full[i], i, t)
+            opt.warmup_step(list(full.unbind(0)), w.lr_at(t))
     torch.cuda.synchronize()
     for rec in recs:
         for key, field in (("x", ob.OB_X), ("m", ob.OB_M), ("v", ob.OB_V)):
             check_sampled("%s chunk %d after warm-up: %s" % (name, rec["chunk"], key),
                           sampled(field, rec), rec["after_warmup"][key])
-    if w.staged:
-        del full
-        torch.cuda.empty_cache()
-        one = torch.empty(w.d, dtype=gdt, device=dev)
 
     for si, t in enumerate(range(w.warmup, w.steps)):
         lr = w.lr_at(t)

@@ -47,16 +47,23 @@ CASES = [
 ]
 
 
-def run_case(d, n, bf16, sigma, warm, comp, staged=False, exact=True, check_every=True):
+def run_case(d, n, bf16, sigma, warm, comp, staged=False, exact=True, check_every=True,
+             staged_warm=False):
     import torch
-    log("case d=%d n=%d bf16=%s warm=%d comp=%d staged=%s" % (d, n, bf16, warm, comp, staged))
+    log("case d=%d n=%d bf16=%s warm=%d comp=%d staged=%s staged_warm=%s"
+        % (d, n, bf16, warm, comp, staged, staged_warm))
     opt = ob.OneBitAdam(d, n, ob.OB_GRAD_BF16 if bf16 else ob.OB_GRAD_F32)
     orc = oracle.Oracle(d, n)
     for t in range(warm + comp):
         hg = host_grads(d, n, t, sigma=sigma, bf16=bf16)
         dg = [to_device_grad(g) for g in hg]
         lr = np.float32(1e-3)
-        if t < warm:
+        if t < warm and staged_warm:
+            for w in range(n):
+                opt.warmup_worker(w, dg[w])
+            opt.warmup_finish(lr)
+            orc.warmup_step(hg, lr)
+        elif t < warm:
             opt.warmup_step(dg, lr)
             orc.warmup_step(hg, lr)
         elif staged:
@@ -70,6 +77,9 @@ def run_case(d, n, bf16, sigma, warm, comp, staged=False, exact=True, check_ever
         torch.cuda.synchronize()
         if check_every or t == warm + comp - 1:
             compare_full(opt, orc, t >= warm, exact=exact, where="step %d" % t)
+        if staged_warm and t < warm:  # the partial sums were cleared from the error slabs
+            for w in range(n):
+                assert not np.any(gpu_np(opt, ob.OB_E_WORKER, w)), "step %d e_w%d" % (t, w)
     return opt, orc
 
 
@@ -80,6 +90,91 @@ def test_parity_small(name, d, n, bf16, sigma, warm, comp):
 
 def test_staged_matches_oracle():
     run_case(4 * 3392, 4, False, 1e-2, 2, 3, staged=True)
+
+
+STAGED_WARM = [
+    # (name, d, n, bf16): worker counts that leave 1, 2, 3 and 4 partial sums
+    ("n1", 1024, 1, False),
+    ("n3", 3 * 1472, 3, False),
+    ("n5_bf16", 5 * 2112, 5, True),
+    ("n7", 7 * 1088, 7, False),
+    ("n8", 8 * 1152, 8, True),
+    ("n11", 11 * 1088, 11, False),
+    ("n64", 64 * 1088, 64, False),
+]
+
+
+@pytest.mark.parametrize("name,d,n,bf16", STAGED_WARM, ids=[c[0] for c in STAGED_WARM])
+def test_staged_warmup_matches_oracle(name, d, n, bf16):
+    """Warm-up gradients one worker at a time (bounded memory) give the same
+    bits as the oracle's pairwise average; the compressed steps after it
+    start from zero errors."""
+    run_case(d, n, bf16, 1e-3 if bf16 else 1e-2, 3, 3, staged=(n % 2 == 1), staged_warm=True)
+
+
+def test_staged_warmup_mixes_with_whole_steps():
+    """Staged and whole warm-up steps in any mix (and a resume between them)."""
+    import torch
+    d, n = 6 * 1152, 6
+    opt = ob.OneBitAdam(d, n)
+    orc = oracle.Oracle(d, n)
+    for t in range(6):
+        hg = host_grads(d, n, t, sigma=1e-2)
+        dg = [to_device_grad(g) for g in hg]
+        lr = np.float32(1e-3)
+        if t in (0, 2):
+            for w in range(n):
+                opt.warmup_worker(w, dg[w])
+            opt.warmup_finish(lr)
+        elif t < 4:
+            opt.warmup_step(dg, lr)
+        else:
+            opt.compressed_step(dg, lr)
+        (orc.warmup_step if t < 4 else orc.compressed_step)(hg, lr)
+        if t == 2:
+            ck = opt.checkpoint()
+            opt = ob.OneBitAdam(d, n, checkpoint=ck)
+        torch.cuda.synchronize()
+        compare_full(opt, orc, t >= 4, exact=True, where="mixed step %d" % t)
+
+
+def test_staged_warmup_phase_rules():
+    import torch
+    d, n = 4096, 4
+    opt = ob.OneBitAdam(d, n)
+    g = [torch.full((d,), 1e-3 * (w + 1), device="cuda") for w in range(n)]
+
+    def refused(fn, *a, status=ob.OB_ERR_PHASE):
+        with pytest.raises(ob.ObAdamError) as e:
+            fn(*a)
+        assert e.value.status == status
+
+    refused(opt.warmup_worker, 1, g[1])  # must start at worker 0
+    refused(opt.warmup_finish, 1e-3)     # nothing open
+    refused(opt.warmup_worker, n, g[0], status=ob.OB_ERR_ARG)
+    opt.warmup_worker(0, g[0])
+    opt.warmup_worker(1, g[1])
+    refused(opt.warmup_worker, 1, g[1])  # twice
+    refused(opt.warmup_worker, 3, g[3])  # skipped worker 2
+    refused(opt.warmup_finish, 1e-3)     # before all workers
+    refused(opt.warmup_step, g, 1e-3)
+    refused(opt.compressed_step, g, 1e-3)
+    refused(opt.compress_worker, 0, g[0])
+    refused(opt.get, ob.OB_E_WORKER, 0, 0, 4)
+    refused(opt.set, ob.OB_V, torch.zeros(4, device="cuda"))
+    refused(opt.checkpoint)
+    opt.warmup_worker(2, g[2])
+    opt.warmup_worker(3, g[3])
+    opt.warmup_finish(1e-3)
+    assert opt.steps == (1, 0)
+    # the gradients were constant: every element saw the same average
+    m = gpu_np(opt, ob.OB_M)
+    want = np.float32(0.1) * (((np.float32(1e-3) + np.float32(2e-3))
+                               + (np.float32(3e-3) + np.float32(4e-3))) / np.float32(4))
+    assert np.all(m == m[0]) and abs(float(m[0]) - float(want)) <= 1e-6 * abs(float(want))
+    opt.compressed_step(g, 1e-3)
+    refused(opt.warmup_worker, 0, g[0])  # warm-up is over
+    assert opt.steps == (2, 1)
 
 
 def test_device_generator_matches_host():
