@@ -95,20 +95,46 @@ __device__ __forceinline__ float pairwise_sum(float* v) {
   return v[0];
 }
 
-// Pairwise sum by levels for any n <= 64 (an odd tail passes up).
-__device__ __forceinline__ float pairwise_sum_any(float* v, int n) {
-  int cnt = n;
-  while (cnt > 1) {
-    int half = cnt >> 1;
-    for (int i = 0; i < half; ++i) v[i] = v[2 * i] + v[2 * i + 1];
-    if (cnt & 1) {
-      v[half] = v[cnt - 1];
-      cnt = half + 1;
-    } else {
-      cnt = half;
+// Pairwise sum by levels of value(0), ..., value(n-1) for any 1 <= n <= 64
+// (an odd tail passes up), in registers.  The values are pushed into a
+// binary-counter stack: level l holds the sum of an aligned block of 2^l
+// values, and value w merges the levels given by the trailing one bits of w
+// (stack level + carry).  The levels left at the end are the set bits of n;
+// folding them from the lowest up (higher level + carry) completes exactly
+// the pairwise-by-levels tree.  Levels are compile-time indices, so nothing
+// goes to scratch memory.
+constexpr int kStackLevels = 7;  // floor(log2(64)) + 1
+
+template <typename F>
+__device__ __forceinline__ float pairwise_sum_stream(int n, F value) {
+  float stack[kStackLevels];
+  for (int w = 0; w < n; ++w) {
+    float v = value(w);
+    int x = w;
+    bool carry = true;
+#pragma unroll
+    for (int l = 0; l < kStackLevels; ++l) {
+      if (carry) {
+        if (x & 1) {
+          v = stack[l] + v;
+          x >>= 1;
+        } else {
+          stack[l] = v;
+          carry = false;
+        }
+      }
     }
   }
-  return v[0];
+  float acc = 0.0f;
+  bool have = false;
+#pragma unroll
+  for (int l = 0; l < kStackLevels; ++l) {
+    if ((n >> l) & 1) {
+      acc = have ? stack[l] + acc : stack[l];
+      have = true;
+    }
+  }
+  return acc;
 }
 
 // ----------------------------------------------------------------- warm-up --
@@ -226,15 +252,14 @@ __global__ void __launch_bounds__(kBlock)
                   float bc2, float lr, float eps) {
   const int64_t stride = (int64_t)gridDim.x * kBlock;
   for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < d; k += stride) {
-    float vals[NW > 0 ? NW : kMaxWorkersPerLaunch];
     float sum;
     if constexpr (NW > 0) {
+      float vals[NW];
 #pragma unroll
       for (int w = 0; w < NW; ++w) vals[w] = grad_value((const GT*)g.p[w], k);
       sum = pairwise_sum<NW>(vals);
     } else {
-      for (int w = 0; w < n; ++w) vals[w] = grad_value((const GT*)g.p[w], k);
-      sum = pairwise_sum_any(vals, n);
+      sum = pairwise_sum_stream(n, [&](int w) { return grad_value((const GT*)g.p[w], k); });
     }
     const float gbar = sum / (float)(NW > 0 ? NW : n);
     float mk = m[k], vk = v[k], xk = x[k];
@@ -429,14 +454,15 @@ __global__ void __launch_bounds__(kBlock)
 template <int NW>
 __device__ __forceinline__ float worker_average(const uint64_t* __restrict__ wbits, int64_t words,
                                                 int64_t row, const float* ws, int n) {
-  float vals[NW > 0 ? NW : kMaxWorkersPerLaunch];
   if constexpr (NW > 0) {
+    float vals[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) vals[w] = signed_scale(wbits[(int64_t)w * words + row], ws[w]);
     return pairwise_sum<NW>(vals) / (float)NW;
   } else {
-    for (int w = 0; w < n; ++w) vals[w] = signed_scale(wbits[(int64_t)w * words + row], ws[w]);
-    return pairwise_sum_any(vals, n) / (float)n;
+    return pairwise_sum_stream(
+               n, [&](int w) { return signed_scale(wbits[(int64_t)w * words + row], ws[w]); }) /
+           (float)n;
   }
 }
 
@@ -546,18 +572,19 @@ __global__ void __launch_bounds__(kBlock)
                   uint64_t* __restrict__ sbits, double* __restrict__ spart) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.y;
-  // per-chunk worker scales in registers for the small-NW paths; the
-  // many-worker path reads them per batch instead
+  // per-chunk worker scales in registers for the few-worker paths; the
+  // many-worker and the run-time-n paths stage them in LDS instead
   constexpr bool BATCHED = NW >= 16;
-  constexpr int WS = BATCHED ? 1 : (NW > 0 ? NW : kMaxWorkersPerLaunch);
+  constexpr bool STAGED = BATCHED || NW == 0;
+  constexpr int WS = STAGED ? 1 : NW;
   float ws[WS];
-  const int nw = NW > 0 ? NW : n;
+  if constexpr (!STAGED) {
 #pragma unroll
-  for (int w = 0; w < WS; ++w)
-    if (w < nw) ws[w] = wscale[w * n + j];
-  __shared__ float sws[BATCHED ? NW : 1];
-  if constexpr (BATCHED) {
-    if ((int)threadIdx.x < NW) sws[threadIdx.x] = wscale[threadIdx.x * n + j];
+    for (int w = 0; w < NW; ++w) ws[w] = wscale[w * n + j];
+  }
+  __shared__ float sws[STAGED ? (NW > 0 ? NW : kMaxWorkersPerLaunch) : 1];
+  if constexpr (STAGED) {
+    if ((int)threadIdx.x < (NW > 0 ? NW : n)) sws[threadIdx.x] = wscale[threadIdx.x * n + j];
     __syncthreads();
   }
   const float sp = sscale_prev[j];
@@ -608,7 +635,7 @@ __global__ void __launch_bounds__(kBlock)
       if constexpr (BATCHED) {
         server_average_rows<NW, 1>(wbits, words, wbase + r, sws, &a);
       } else {
-        a = worker_average<NW>(wbits, words, wbase + r, ws, n);
+        a = worker_average<NW>(wbits, words, wbase + r, NW == 0 ? sws : ws, n);
       }
       const float uv = a + e;
       u[k] = uv;

@@ -3,7 +3,8 @@
 Sizes are chosen so the oracle finishes in seconds while the kernels see
 several segments, a ragged last segment (chunk length not a multiple of
 1024), chunks shorter than one segment, more segment partials than one
-finalize pass folds, the generic (non power of two) worker count, bf16
+finalize pass folds, generic (non power of two) worker counts with 2 to 4
+levels of partial sums left for the final fold, bf16
 gradients, the first compressed step (fp32 momentum) and later ones
 (momentum kept as server sign words)."""
 import numpy as np
@@ -42,6 +43,9 @@ CASES = [
     ("n32_workers", 32 * 2112, 32, True, 1e-3, 2, 3),
     ("n6_generic", 6 * 1152, 6, False, 1e-2, 1, 3),
     ("n7_generic", 7 * 1088, 7, False, 1e-2, 1, 3),
+    ("n11_generic", 11 * 1088, 11, False, 1e-2, 2, 3),
+    ("n24_generic_bf16", 24 * 1152, 24, True, 1e-3, 2, 3),
+    ("n48_generic", 48 * 1088, 48, False, 1e-3, 1, 3),
     ("n2_two_fold_groups", 2 * 614976, 2, False, 1e-2, 1, 3),
     ("n1_eight_fold_groups", 3072064, 1, True, 1e-3, 1, 2),
 ]
