@@ -79,12 +79,44 @@ def load_traffic(workload):
     return t
 
 
+def host_cpu():
+    """The host's CPU model and the cores this process may use."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w, steps=1):
     """The CPU oracle on chunk 0 (all n workers, 1/n of the step's work),
-    timed over `steps` compressed steps after the warm-up, scaled by n."""
+    timed over `steps` compressed steps after the warm-up, scaled by n.  The
+    calling thread is pinned to one core while the oracle runs."""
     import oracle
     from synth import workloads as W
     L = w.L
+    model, usable = host_cpu()
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        per_step = _oracle_step_seconds(oracle, W, w, L, steps)
+    finally:
+        os.sched_setaffinity(0, allowed)
+    return {"value": w.n * w.d / per_step, "unit": "params*workers/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "chunk 0 of %d (%d elements x %d workers), %d compressed step(s) after "
+                      "%d warm-up steps, single thread pinned to core %d, time x%d for the "
+                      "whole step" % (w.n, L, w.n, steps, w.warmup, core, w.n),
+            "host_cpu": model, "host_cores_usable": usable,
+            "s_per_step_extrapolated": per_step}
+
+
+def _oracle_step_seconds(oracle, W, w, L, steps):
     o = oracle.Oracle(w.d, w.n, w.beta1, w.beta2, w.eps, j0=0, j1=1, keep_debug=False)
     secs = []
     for t in range(w.warmup + steps):
@@ -96,13 +128,7 @@ def cpu_baseline(w, steps=1):
         o.compressed_step(g, w.lr_at(t))
         secs.append(time.perf_counter() - t0)
     o.close()
-    per_step = sum(secs) / len(secs) * w.n
-    return {"value": w.n * w.d / per_step, "unit": "params*workers/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "chunk 0 of %d (%d elements x %d workers), %d compressed step(s) after "
-                      "%d warm-up steps, single thread, time x%d for the whole step"
-                      % (w.n, L, w.n, steps, w.warmup, w.n),
-            "s_per_step_extrapolated": per_step}
+    return sum(secs) / len(secs) * w.n
 
 
 PROBE_LIB = os.path.join(ROOT, "communication_compressed_distributed_02_amd", "libob_probe.so")
@@ -322,6 +348,11 @@ def main():
                  "fp32_momentum_bytes": fp32_momentum_step_bytes(w),
                  "fp32_momentum_frac_of_peak": round(
                      fp32_momentum_step_bytes(w) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "traffic": traffic.get("step_bytes") if traffic else None,
+                 "traffic_GB_s": round(traffic["step_bytes"] / (ms_step * 1e-3) / 1e9, 1)
+                 if traffic and traffic.get("step_bytes") else None,
+                 "traffic_unit": "HBM bytes per steady-state step (rocprofv3 FETCH_SIZE + "
+                                 "WRITE_SIZE of each kernel, copy-calibrated)",
                  "wall_s": round(wall, 4),
                  "ms_per_step_with_kernel_events": round(ms_step_timed, 4),
                  "timing_launches_dropped": dropped},
