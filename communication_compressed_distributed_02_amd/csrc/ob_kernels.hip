@@ -451,6 +451,11 @@ __global__ void __launch_bounds__(kBlock)
 // Server j: a = pairwise over workers of (bit ? s_wj : -s_wj) / n;
 // u = a + (u_prev - (u_prev >= 0 ? s_prev : -s_prev)); stores u, sign words,
 // segment partials.  grid.y = chunk; grid.x strides over segments.
+//
+// Two forms: few workers (n = 1, 2, 4, or a count that is not a power of
+// two) read the sign words as uniform scalar loads and select +-s per worker;
+// n = 8, 16, 32, 64 use the group tables below.
+
 template <int NW>
 __device__ __forceinline__ float worker_average(const uint64_t* __restrict__ wbits, int64_t words,
                                                 int64_t row, const float* ws, int n) {
@@ -466,7 +471,7 @@ __device__ __forceinline__ float worker_average(const uint64_t* __restrict__ wbi
   }
 }
 
-// Full segment, NW a power of two: the 16 sign words of one worker are one
+// Full segment, NW = 1, 2 or 4: the 16 sign words of one worker are one
 // uniform 128-byte burst; workers are folded into per-row stacks in worker
 // order so that the result is exactly the pairwise-by-levels sum (merging
 // level l whenever bit l of the worker index is set, left operand first).
@@ -474,8 +479,8 @@ template <int NW>
 __device__ __forceinline__ void server_average_segment(const uint64_t* __restrict__ wbits,
                                                        int64_t words, int64_t wbase,
                                                        const float* ws, float* avg) {
-  constexpr int LEVELS = NW == 1 ? 1 : (NW == 2 ? 2 : NW == 4 ? 3 : NW == 8 ? 4 : NW == 16 ? 5
-                                        : NW == 32 ? 6 : 7);
+  constexpr int LEVELS = NW == 1 ? 1 : (NW == 2 ? 2 : 3);
+  static_assert(NW == 1 || NW == 2 || NW == 4, "few-worker path");
   float stack[LEVELS][kSegRows];
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -496,74 +501,7 @@ __device__ __forceinline__ void server_average_segment(const uint64_t* __restric
   for (int r = 0; r < kSegRows; ++r) avg[r] = stack[LEVELS - 1][r] / (float)NW;
 }
 
-// Many workers (NW >= 16, a power of two): R rows at a time, workers in
-// batches of B (one burst of B scalar loads per batch, the B-worker subtree
-// formed in registers), batches folded into per-row stacks in batch order --
-// again exactly the pairwise-by-levels sum -- with the stack levels as
-// compile-time indices under a uniform run-time batch loop, which keeps the
-// register footprint (and so the occupancy) from growing with NW.
-constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
-
-// Batch shape by worker count (measured): 16 workers -> batches of 2 over a
-// whole segment (server pass 1.09 -> 0.92 ms on 334M x 16); 32+ workers ->
-// batches of 4 over 8 rows (5.26 -> 2.15 ms on 340M x 64).
-template <int NW>
-struct ServerBatch {
-  static constexpr int workers = NW == 16 ? 2 : 4;
-  static constexpr int rows = NW == 16 ? kSegRows : 8;
-};
-
-template <int NW, int R, int B = ServerBatch<NW>::workers>
-__device__ __forceinline__ void server_average_rows(const uint64_t* __restrict__ wbits,
-                                                    int64_t words, int64_t wbase,
-                                                    const float* sws, float* avg) {
-  constexpr int NB = NW / B;
-  constexpr int LB = ilog2(NB) + 1;
-  static_assert(NW >= 8 && NW <= 128 && (NW & (NW - 1)) == 0, "power of two, 8..128");
-  static_assert(B == 2 || B == 4 || B == 8, "batch of 2, 4 or 8 workers");
-  // (used from NW = 32 on: at 16 workers the fully unrolled segment path is faster)
-  float stack[LB][R];
-#pragma unroll 1
-  for (int b = 0; b < NB; ++b) {
-    float s[B];
-    uint64_t wd[B][R];
-#pragma unroll
-    for (int q = 0; q < B; ++q) {
-      const int w = b * B + q;
-      s[q] = sws[w];  // this chunk's worker scales, staged in LDS
-      const uint64_t* __restrict__ p = wbits + (int64_t)w * words + wbase;
-#pragma unroll
-      for (int r = 0; r < R; ++r) wd[q][r] = p[r];
-    }
-    float v[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float a[B];
-#pragma unroll
-      for (int q = 0; q < B; ++q) a[q] = signed_scale(wd[q][r], s[q]);
-      v[r] = pairwise_sum<B>(a);  // the batch is an aligned subtree of the worker tree
-    }
-    int x = b;
-    bool carry = true;
-#pragma unroll
-    for (int lvl = 0; lvl < LB; ++lvl) {
-      if (carry) {
-        if (x & 1) {
-#pragma unroll
-          for (int r = 0; r < R; ++r) v[r] = stack[lvl][r] + v[r];
-          x >>= 1;
-        } else {
-#pragma unroll
-          for (int r = 0; r < R; ++r) stack[lvl][r] = v[r];
-          carry = false;
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) avg[r] = stack[LB - 1][r] / (float)NW;
-}
-
+// NW = 1, 2, 4, or 0 for a run-time worker count.
 template <int NW>
 __global__ void __launch_bounds__(kBlock)
     server_kernel(int64_t L, int n, int64_t nseg, int64_t words,
@@ -572,19 +510,17 @@ __global__ void __launch_bounds__(kBlock)
                   uint64_t* __restrict__ sbits, double* __restrict__ spart) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.y;
-  // per-chunk worker scales in registers for the few-worker paths; the
-  // many-worker and the run-time-n paths stage them in LDS instead
-  constexpr bool BATCHED = NW >= 16;
-  constexpr bool STAGED = BATCHED || NW == 0;
-  constexpr int WS = STAGED ? 1 : NW;
+  // per-chunk worker scales: in registers for a compile-time count, staged
+  // in LDS for a run-time one
+  constexpr int WS = NW > 0 ? NW : 1;
   float ws[WS];
-  if constexpr (!STAGED) {
+  if constexpr (NW > 0) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) ws[w] = wscale[w * n + j];
   }
-  __shared__ float sws[STAGED ? (NW > 0 ? NW : kMaxWorkersPerLaunch) : 1];
-  if constexpr (STAGED) {
-    if ((int)threadIdx.x < (NW > 0 ? NW : n)) sws[threadIdx.x] = wscale[threadIdx.x * n + j];
+  __shared__ float sws[NW > 0 ? 1 : kMaxWorkersPerLaunch];
+  if constexpr (NW == 0) {
+    if ((int)threadIdx.x < n) sws[threadIdx.x] = wscale[threadIdx.x * n + j];
     __syncthreads();
   }
   const float sp = sscale_prev[j];
@@ -604,14 +540,7 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
         for (int r = 0; r < kSegRows; ++r) up[r] = ld_stream(u + base + 64 * r + lane);
         float avg[kSegRows];
-        if constexpr (BATCHED) {
-          constexpr int RB = ServerBatch<NW>::rows;
-#pragma unroll
-          for (int h = 0; h < kSegRows / RB; ++h)
-            server_average_rows<NW, RB>(wbits, words, wbase + h * RB, sws, avg + h * RB);
-        } else {
-          server_average_segment<NW>(wbits, words, wbase, ws, avg);
-        }
+        server_average_segment<NW>(wbits, words, wbase, ws, avg);
 #pragma unroll
         for (int r = 0; r < kSegRows; ++r) {
           const float e = up[r] - (up[r] >= 0.0f ? sp : -sp);
@@ -631,17 +560,181 @@ __global__ void __launch_bounds__(kBlock)
       const int64_t k = base + 64 * r + lane;
       const float up = u[k];
       const float e = up - (up >= 0.0f ? sp : -sp);
-      float a;
-      if constexpr (BATCHED) {
-        server_average_rows<NW, 1>(wbits, words, wbase + r, sws, &a);
-      } else {
-        a = worker_average<NW>(wbits, words, wbase + r, NW == 0 ? sws : ws, n);
-      }
+      const float a = worker_average<NW>(wbits, words, wbase + r, NW == 0 ? sws : ws, n);
       const float uv = a + e;
       u[k] = uv;
       const uint64_t word = __ballot(uv >= 0.0f);
       mine = lane == r ? word : mine;
       acc = add_square(acc, uv);
+    }
+    acc = butterfly(acc);
+    if (lane < rows) sbits[wbase + lane] = mine;
+    if (lane == 0) spart[(int64_t)j * nseg + s] = acc;
+  }
+}
+
+// ------------------------------------- server pass, 8 to 64 workers ----
+// n = 8*NG workers.  Workers 8g..8g+7 form an aligned subtree of the
+// pairwise tree, so their sum for one element depends only on their 8 sign
+// bits: each block tabulates, in LDS, the 256 possible subtree sums of every
+// group for its chunk's scales (each entry formed in the pairwise order).
+// The sign words are read with vector loads: for 8 rows, lane 8r + q loads
+// worker 8g + q's word of row r, and a 64x64 bit transpose across the wave
+// leaves in lane e, byte r, the group's 8 sign bits of element e of row r --
+// a table index.  The NG group sums are then added pairwise.  (The scalar
+// form needs one scalar load of 64 bytes per worker and 8 rows, and scalar
+// loads do not overlap: with many workers it was bound by them.)
+
+// Value of x in lane (lane ^ K).
+template <int K>
+__device__ __forceinline__ uint32_t xor_fetch(uint32_t x, int lane) {
+  if constexpr (K == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+  } else if constexpr (K == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+  } else if constexpr (K == 4 || K == 8 || K == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (K << 10));  // xor within 32
+  } else {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ K) << 2, (int)x);
+  }
+}
+
+// One exchange stage of the transpose for one 32-bit half: bit K of the bit
+// position swaps with bit K of the lane.  Lanes with bit K clear keep the
+// positions with bit K clear and take the partner's others shifted up by K;
+// lanes with bit K set keep the positions with bit K set and take the
+// partner's others shifted down by K (as rotations: the wrapped bits fall on
+// kept positions).
+template <int K>
+__device__ __forceinline__ uint32_t transpose_stage(uint32_t x, int lane) {
+  constexpr uint32_t kHigh = K == 16 ? 0xFFFF0000u
+                             : K == 8 ? 0xFF00FF00u
+                             : K == 4 ? 0xF0F0F0F0u
+                             : K == 2 ? 0xCCCCCCCCu
+                                      : 0xAAAAAAAAu;
+  const bool upper = (lane & K) != 0;
+  const uint32_t p = xor_fetch<K>(x, lane);
+  const uint32_t r = __builtin_amdgcn_alignbit(p, p, upper ? K : 32 - K);
+  const uint32_t keep = upper ? kHigh : ~kHigh;
+  return (x & keep) | (r & ~keep);
+}
+
+// 64x64 bit transpose across the wave.  On entry lane L holds row L of the
+// matrix as (lo, hi) = bits 0..31 and 32..63; on exit lane e holds column e:
+// bit L of (lo, hi) is bit e of row L.  (Every stage swaps one bit of the
+// row index with the same bit of the column index; their order is free.)
+__device__ __forceinline__ void transpose64(uint32_t& lo, uint32_t& hi, int lane) {
+  const uint32_t a = xor_fetch<32>(lo, lane);
+  const uint32_t b = xor_fetch<32>(hi, lane);
+  if (lane < 32) hi = a; else lo = b;
+  lo = transpose_stage<16>(lo, lane);
+  hi = transpose_stage<16>(hi, lane);
+  lo = transpose_stage<8>(lo, lane);
+  hi = transpose_stage<8>(hi, lane);
+  lo = transpose_stage<4>(lo, lane);
+  hi = transpose_stage<4>(hi, lane);
+  lo = transpose_stage<2>(lo, lane);
+  hi = transpose_stage<2>(hi, lane);
+  lo = transpose_stage<1>(lo, lane);
+  hi = transpose_stage<1>(hi, lane);
+}
+
+// Server average of rows 0..nrows-1 (nrows <= 8 used) starting at sign word
+// `wrow0`, for lane's element: avg[r].  One worker's 16 words of a segment are
+// one 128-byte line read in two halves, so these are ordinary loads (kept in
+// L2 for the second half; non-temporal ones were 25 % slower).
+template <int NG>
+__device__ __forceinline__ void server_average_groups(const uint64_t* __restrict__ wbits,
+                                                      int64_t words, int64_t wrow0, int nrows,
+                                                      const float* tab, int lane, float* avg) {
+  uint32_t lo[NG], hi[NG];
+  const int q = lane & 7, r = lane >> 3;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    uint64_t wd = 0;
+    if (r < nrows) wd = wbits[(int64_t)(8 * g + q) * words + wrow0 + r];
+    lo[g] = (uint32_t)wd;
+    hi[g] = (uint32_t)(wd >> 32);
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) transpose64(lo[g], hi[g], lane);
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    float o[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const uint32_t half = rr < 4 ? lo[g] : hi[g];
+      o[g] = tab[g * 256 + __builtin_amdgcn_ubfe(half, 8 * (rr & 3), 8)];
+    }
+    avg[rr] = pairwise_sum<NG>(o) / (float)(8 * NG);
+  }
+}
+
+template <int NG>
+__global__ void __launch_bounds__(kBlock)
+    server_groups_kernel(int64_t L, int n, int64_t nseg, int64_t words,
+                         const uint64_t* __restrict__ wbits, const float* __restrict__ wscale,
+                         float* __restrict__ u, const float* __restrict__ sscale_prev,
+                         uint64_t* __restrict__ sbits, double* __restrict__ spart) {
+  __shared__ float tab[NG * 256];
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.y;
+  for (int t = threadIdx.x; t < NG * 256; t += kBlock) {
+    const int g = t >> 8, i = t & 255;
+    float v[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const float sc = wscale[(8 * g + b) * n + j];
+      v[b] = ((i >> b) & 1) ? sc : -sc;
+    }
+    tab[t] = pairwise_sum<8>(v);
+  }
+  __syncthreads();
+  const float sp = sscale_prev[j];
+  const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); s < nseg;
+       s += nwave) {
+    const int64_t q0 = s * kSegElems;
+    const int64_t left = (L - q0) >> 6;
+    const int rows = left < kSegRows ? (int)left : kSegRows;
+    const int64_t base = (int64_t)j * L + q0;
+    const int64_t wbase = base >> 6;
+    double acc = 0.0;
+    uint64_t mine = 0;
+#pragma unroll
+    for (int h = 0; h < kSegRows / 8; ++h) {
+      const int nrows = rows - 8 * h;  // rows of this half (<= 0 past a chunk's end)
+      if (nrows <= 0) break;
+      float avg[8];
+      server_average_groups<NG>(wbits, words, wbase + 8 * h, nrows, tab, lane, avg);
+      if (nrows >= 8) {
+        float up[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) up[r] = ld_stream(u + base + 64 * (8 * h + r) + lane);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float e = up[r] - (up[r] >= 0.0f ? sp : -sp);
+          const float uv = avg[r] + e;
+          st_stream(u + base + 64 * (8 * h + r) + lane, uv);
+          const uint64_t word = __ballot(uv >= 0.0f);
+          mine = lane == 8 * h + r ? word : mine;
+          acc = add_square(acc, uv);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          if (r < nrows) {
+            const int64_t k = base + 64 * (8 * h + r) + lane;
+            const float up = u[k];
+            const float e = up - (up >= 0.0f ? sp : -sp);
+            const float uv = avg[r] + e;
+            u[k] = uv;
+            const uint64_t word = __ballot(uv >= 0.0f);
+            mine = lane == 8 * h + r ? word : mine;
+            acc = add_square(acc, uv);
+          }
+        }
+      }
     }
     acc = butterfly(acc);
     if (lane < rows) sbits[wbase + lane] = mine;
@@ -894,6 +987,23 @@ hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t
 }
 
 hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (s.n == 8 || s.n == 16 || s.n == 32 || s.n == 64) {
+    // segments per wave (measured): 1 up to 16 workers, 4 beyond (the tables
+    // are built once per block)
+    const int per_wave = s.n <= 16 ? 1 : 4;
+    const dim3 grid(grid_for(s.nseg, kWavesPerBlock * per_wave, kMaxBlocksPerRow), (unsigned)s.n);
+#define OB_SRVG(NG)                                                                            \
+  return launch(server_groups_kernel<NG>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n, s.nseg, \
+                s.words, (const uint64_t*)s.wbits, (const float*)s.wscale, s.u,                 \
+                (const float*)s.sscale, s.sbits, s.spart)
+    switch (s.n) {
+      case 8: OB_SRVG(1);
+      case 16: OB_SRVG(2);
+      case 32: OB_SRVG(4);
+      default: OB_SRVG(8);
+    }
+#undef OB_SRVG
+  }
   const dim3 grid(grid_for(s.nseg, kWavesPerBlock, kMaxBlocksPerRow), (unsigned)s.n);
 #define OB_SRV(NW)                                                                             \
   return launch(server_kernel<NW>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n, s.nseg,       \
@@ -903,10 +1013,6 @@ hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0,
     case 1: OB_SRV(1);
     case 2: OB_SRV(2);
     case 4: OB_SRV(4);
-    case 8: OB_SRV(8);
-    case 16: OB_SRV(16);
-    case 32: OB_SRV(32);
-    case 64: OB_SRV(64);
     default: OB_SRV(0);
   }
 #undef OB_SRV
