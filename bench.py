@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -59,7 +60,14 @@ def fp32_momentum_step_bytes(w):
 
 
 def kernel_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source's code: // comments, indentation and
+    blank lines removed, so that only a change of code voids the counters."""
+    code = []
+    for line in open(KERNEL_SRC, encoding="utf-8"):
+        line = re.sub(r"//.*$", "", line).strip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def load_traffic(workload):

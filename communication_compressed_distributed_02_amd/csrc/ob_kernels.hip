@@ -23,16 +23,20 @@
 //  - After the first compressed step the momentum is exactly the
 //    decompressed server output, so it is kept as the server's sign words and
 //    per-chunk scales (1/8 byte per element instead of 4 read + 4 written).
-//  - Sign words are read with scalar (uniform) loads and decoded with an
-//    inverse ballot: bit `lane` of a uniform 64-bit word selects +s or -s in
-//    one v_cndmask.
-//  - The grid is non-persistent (one wave per segment, grid.y = worker x
-//    chunk): persistent grids and several segments per wave measured slower.
-//  - The server folds the workers' +-s in worker order into per-row stacks
-//    that reproduce the pairwise-by-levels sum exactly; from 32 workers on it
-//    works 8 rows at a time over batches of 4 workers to bound registers.
-//  - Per-chunk scales come from two small kernels: aligned groups of 512
-//    segment partials folded in parallel, then one block per chunk.
+//  - The momentum's sign words are read with scalar (uniform) loads and
+//    decoded with an inverse ballot: bit `lane` of a uniform 64-bit word
+//    selects +s or -s in one v_cndmask.
+//  - The worker grid is non-persistent (one wave per segment, grid.y =
+//    worker x chunk): persistent grids and several segments per wave
+//    measured slower.
+//  - The server pass for 8 to 64 workers looks up sums of 8-worker subtrees
+//    in LDS tables, indexed by the sign bits that a cross-lane bit transpose
+//    of vector-loaded sign words puts in each lane; for other worker counts
+//    it folds the workers' +-s in worker order into per-row stacks.  Both
+//    reproduce the pairwise-by-levels sum exactly.
+//  - Per-chunk scales come from small kernels: one dispatch that folds a
+//    chunk's segment partials in registers and one block, or aligned groups
+//    of 512 partials folded in parallel and then one block per chunk.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
