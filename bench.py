@@ -21,6 +21,8 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -100,10 +102,12 @@ def host_cpu():
     return model, len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, steps=1):
+def cpu_baseline(w, steps=1, snap=None):
     """The CPU oracle on chunk 0 (all n workers, 1/n of the step's work),
     timed over `steps` compressed steps after the warm-up, scaled by n.  The
-    calling thread is pinned to one core while the oracle runs."""
+    calling thread is pinned to one core while the oracle runs.  With `snap`
+    (the GPU's chunk-0 state after the same steps on the same gradients) the
+    two are compared: returns (baseline, parity)."""
     import oracle
     from synth import workloads as W
     L = w.L
@@ -112,16 +116,64 @@ def cpu_baseline(w, steps=1):
     core = min(allowed)
     os.sched_setaffinity(0, {core})
     try:
-        per_step = _oracle_step_seconds(oracle, W, w, L, steps)
+        per_step, o = _oracle_step_seconds(oracle, W, w, L, steps)
     finally:
         os.sched_setaffinity(0, allowed)
+    parity = compare_chunk0(oracle, o, snap, w) if snap is not None else None
+    o.close()
     return {"value": w.n * w.d / per_step, "unit": "params*workers/s", "cores": 1,
             "kind": "oracle",
             "sample": "chunk 0 of %d (%d elements x %d workers), %d compressed step(s) after "
                       "%d warm-up steps, single thread pinned to core %d, time x%d for the "
                       "whole step" % (w.n, L, w.n, steps, w.warmup, core, w.n),
             "host_cpu": model, "host_cores_usable": usable,
-            "s_per_step_extrapolated": per_step}
+            "s_per_step_extrapolated": per_step}, parity
+
+
+REL_TOL, ABS_TOL = 1e-5, 1e-6
+
+
+def snapshot_chunk0(opt, w):
+    """The GPU's state of chunk 0 (host copies) for compare_chunk0."""
+    from communication_compressed_distributed_02_amd import ob_adam as ob
+    L, n = w.L, w.n
+
+    def get(field, worker=0, count=L):
+        return opt.get(field, worker, 0, count).cpu().numpy()
+    return {"step": opt.steps[0],
+            "x": get(ob.OB_X), "e_srv": get(ob.OB_E_SERVER),
+            "e_w": [get(ob.OB_E_WORKER, i) for i in range(n)],
+            "bits_w": [get(ob.OB_BITS_WORKER, i, L // 64).view(np.uint64) for i in range(n)],
+            "bits_s": get(ob.OB_BITS_SERVER, 0, L // 64).view(np.uint64),
+            "scale_w": [get(ob.OB_SCALE_WORKER, i, 1).view(np.uint32)[0] for i in range(n)],
+            "scale_s": get(ob.OB_SCALE_SERVER, 0, 1).view(np.uint32)[0]}
+
+
+def compare_chunk0(oracle, o, snap, w):
+    """Sign words, scales and the step counter bit-exact; x and the errors
+    within 1e-5 relative or 1e-6 absolute (worst ratio of error to the
+    allowed error reported; <= 1 passes)."""
+    n = w.n
+    bits = all(np.array_equal(snap["bits_w"][i], o._view(oracle.BITS_WORKER, i))
+               for i in range(n)) and np.array_equal(snap["bits_s"], o._view(oracle.BITS_SERVER))
+    scales = (all(snap["scale_w"][i] == o._view(oracle.SCALE_WORKER, i)[:1].view(np.uint32)[0]
+                  for i in range(n))
+              and snap["scale_s"] == o._view(oracle.SCALE_SERVER)[:1].view(np.uint32)[0])
+    worst = {}
+    fields = [("x", snap["x"], o._view(oracle.X)), ("e_srv", snap["e_srv"], o._view(oracle.E_SERVER))]
+    fields += [("e_w%d" % i, snap["e_w"][i], o._view(oracle.E_WORKER, i)) for i in range(n)]
+    for name, g, r in fields:
+        g64 = g.astype(np.float64)
+        r64 = r.astype(np.float64)
+        allowed = np.maximum(REL_TOL * np.abs(r64), ABS_TOL)
+        worst[name] = float(np.max(np.abs(g64 - r64) / allowed))
+    ratio = max(worst.values())
+    return {"against": "oracle", "sample": "chunk 0 (%d elements x %d workers), state after "
+            "step %d" % (w.L, n, o.step), "step_equal": snap["step"] == o.step,
+            "sign_words_equal": bool(bits), "scales_equal": bool(scales),
+            "fp32_worst_error_over_tolerance": ratio,
+            "fp32_worst_field": max(worst, key=worst.get),
+            "pass": bool(bits and scales and snap["step"] == o.step and ratio <= 1.0)}
 
 
 def _oracle_step_seconds(oracle, W, w, L, steps):
@@ -135,8 +187,7 @@ def _oracle_step_seconds(oracle, W, w, L, steps):
         t0 = time.perf_counter()
         o.compressed_step(g, w.lr_at(t))
         secs.append(time.perf_counter() - t0)
-    o.close()
-    return sum(secs) / len(secs) * w.n
+    return sum(secs) / len(secs) * w.n, o
 
 
 PROBE_LIB = os.path.join(ROOT, "communication_compressed_distributed_02_amd", "libob_probe.so")
@@ -219,7 +270,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3, help="untimed compressed steps")
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--cpu-steps", type=int, default=None,
+                    help="compressed steps of the CPU baseline (default: --warmup, so that "
+                         "its state can be compared with the GPU's after the untimed steps)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's device copy of MIB MiB five times (a kernel of "
                          "known traffic for scaling profiler byte counters) and exit")
@@ -279,6 +332,13 @@ def main():
     for t in range(w.warmup, w.warmup + a.warmup):
         step(opt, t)
     torch.cuda.synchronize()
+    cpu_steps = a.warmup if a.cpu_steps is None else a.cpu_steps
+    snap = None
+    if not a.no_cpu_baseline and cpu_steps == a.warmup and ring >= w.warmup + a.warmup:
+        # the untimed steps ran on each step's own gradients: keep chunk 0's
+        # state for the comparison with the oracle after the same steps
+        snap = snapshot_chunk0(opt, w)
+        torch.cuda.synchronize()
     print("# timing %d compressed steps" % a.steps, file=sys.stderr, flush=True)
 
     # Region 1 (the headline): K steps with nothing but the step on the stream.
@@ -376,9 +436,10 @@ def main():
     result["ceilings"] = ceil
     if not a.no_cpu_baseline:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, a.cpu_steps)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(w, cpu_steps, snap)
     else:
         result["cpu_baseline"] = None
+        result["parity"] = None
     print(json.dumps(result), flush=True)
 
 
