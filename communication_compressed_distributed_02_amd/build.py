@@ -39,6 +39,19 @@ def build_probe(out=PROBE_LIB):
     return out
 
 
+MATHCHECK_LIB = os.path.join(PKG, "libob_mathcheck.so")
+MATHCHECK_SOURCES = [os.path.join(CSRC, "ob_mathcheck.hip")]
+
+
+def build_mathcheck(out=MATHCHECK_LIB):
+    """Elementwise checks of the step's floating-point environment (tests)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC] + FLAGS + MATHCHECK_SOURCES + ["-o", tmp])
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build())
     print(build_probe())
+    print(build_mathcheck())

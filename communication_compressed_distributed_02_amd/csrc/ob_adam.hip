@@ -14,6 +14,8 @@
 
 struct ob_adam_handle {
   ob::State st;
+  char* base;           // the caller's workspace
+  ob::Layout layout;
   hipStream_t stream;
   int64_t steps;        // warm-up + compressed steps taken
   int64_t compressed;   // compressed steps taken
@@ -152,6 +154,8 @@ ob_adam_handle* make_handle(const ob_adam_config* cfg, void* workspace, void* st
   ob_adam_handle* h = new (std::nothrow) ob_adam_handle();
   if (h == nullptr) return nullptr;
   char* base = (char*)workspace;
+  h->base = base;
+  h->layout = l;
   ob::State& s = h->st;
   s.d = cfg->d;
   s.n = cfg->n_workers;
@@ -199,6 +203,9 @@ ob_status ob_adam_init(const ob_adam_config* cfg, void* workspace, uint64_t ws_b
   const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers);
   const ob::State& s = h->st;
   hipError_t e = hipMemsetAsync(workspace, 0, l.total, h->stream);
+  for (int i = 0; i < ob::kNumGuards && e == hipSuccess; ++i)
+    e = hipMemsetD32Async((hipDeviceptr_t)(h->base + l.guard[i]), (int)ob::guard_word(i),
+                          ob::kGuardBytes / 4, h->stream);
   if (e == hipSuccess && x0 != nullptr)
     e = hipMemcpyAsync(s.x, x0, sizeof(float) * (size_t)s.d, hipMemcpyDeviceToDevice, h->stream);
   if (e != hipSuccess) {
@@ -411,6 +418,26 @@ ob_status ob_adam_set_state(ob_adam_t h, int32_t field, int64_t offset, int64_t 
   if (src_device == nullptr) return OB_ERR_ARG;
   return fail(h, hipMemcpyAsync(dst + offset, src_device, sizeof(float) * (size_t)count,
                                 hipMemcpyDeviceToDevice, h->stream));
+}
+
+ob_status ob_adam_check_guards(ob_adam_t h, int32_t* first_bad) {
+  if (h == nullptr || first_bad == nullptr) return OB_ERR_ARG;
+  if (h->poisoned) return OB_ERR_HIP;
+  if (hipStreamSynchronize(h->stream) != hipSuccess) return fail(h, hipErrorUnknown);
+  uint32_t words[ob::kGuardBytes / 4];
+  *first_bad = -1;
+  for (int i = 0; i < ob::kNumGuards; ++i) {
+    if (hipMemcpy(words, h->base + h->layout.guard[i], ob::kGuardBytes,
+                  hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(h, hipErrorUnknown);
+    for (uint64_t k = 0; k < ob::kGuardBytes / 4; ++k) {
+      if (words[k] != ob::guard_word(i)) {
+        *first_bad = i;
+        return OB_OK;
+      }
+    }
+  }
+  return OB_OK;
 }
 
 ob_status ob_adam_params(ob_adam_t h, float** x_device) {

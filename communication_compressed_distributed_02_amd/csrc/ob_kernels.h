@@ -38,8 +38,16 @@ struct State {
 };
 
 // Workspace layout: byte offsets of each buffer (256-byte aligned) and total.
+// Every sub-buffer is followed directly by a guard region of kGuardBytes
+// holding a known pattern (guard i: 32-bit words guard_word(i)), so that a
+// write past a buffer's end can be detected from the host.
+constexpr int kNumGuards = 12;
+constexpr uint64_t kGuardBytes = 256;
+constexpr uint32_t guard_word(int i) { return 0xA5C30000u + (uint32_t)i; }
+
 struct Layout {
   uint64_t x, m, v, u, c, wbits, sbits, wpart, spart, fold, wscale, sscale, total;
+  uint64_t guard[kNumGuards];  // offsets of the guards, in workspace order
 };
 Layout layout_for(int64_t d, int n);
 

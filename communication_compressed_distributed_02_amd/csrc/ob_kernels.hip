@@ -841,9 +841,11 @@ Layout layout_for(int64_t d, int n) {
   const uint64_t ud = (uint64_t)d, un = (uint64_t)n;
   const uint64_t nseg = (uint64_t)((d / n + kSegElems - 1) / kSegElems);
   uint64_t off = 0;
+  int ng = 0;
   auto take = [&](uint64_t bytes) {
-    uint64_t at = off;
-    off = align256(off + bytes);
+    const uint64_t at = off;
+    l.guard[ng++] = at + bytes;  // right after the buffer (4-byte aligned)
+    off = align256(at + bytes + kGuardBytes);
     return at;
   };
   l.x = take(4 * ud);

@@ -23,7 +23,7 @@ EXPORTED = ("ob_adam_workspace_bytes", "ob_adam_init", "ob_adam_warmup_step",
             "ob_adam_warmup_worker", "ob_adam_warmup_finish",
             "ob_adam_compressed_step", "ob_adam_compress_worker", "ob_adam_compressed_finish",
             "ob_adam_get_state", "ob_adam_set_state", "ob_adam_params", "ob_adam_step_count",
-            "ob_adam_get_counters", "ob_adam_attach", "ob_adam_set_timing",
+            "ob_adam_get_counters", "ob_adam_attach", "ob_adam_check_guards", "ob_adam_set_timing",
             "ob_adam_kernel_times", "ob_adam_destroy", "ob_status_str")
 KERNELS = ("warmup", "worker", "worker_scale", "server", "server_scale", "update")
 
@@ -65,6 +65,7 @@ def _load(path=LIB_PATH):
         "ob_adam_params": [P, ctypes.POINTER(P)],
         "ob_adam_get_counters": [P, ctypes.POINTER(ob_adam_counters)],
         "ob_adam_attach": [cfgp, P, U64, ctypes.POINTER(ob_adam_counters), P, ctypes.POINTER(P)],
+        "ob_adam_check_guards": [P, ctypes.POINTER(I32)],
         "ob_adam_step_count": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "ob_adam_set_timing": [P, I32],
         "ob_adam_kernel_times": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64),
@@ -156,6 +157,13 @@ def ob_adam_get_counters(h):
     c = ob_adam_counters()
     _check(_lib.ob_adam_get_counters(h, ctypes.byref(c)), "ob_adam_get_counters")
     return (c.steps, c.compressed_steps, c.warmup_steps)
+
+
+def ob_adam_check_guards(h):
+    """-1 if every workspace guard is intact, else the first changed one."""
+    bad = ctypes.c_int32(0)
+    _check(_lib.ob_adam_check_guards(h, ctypes.byref(bad)), "ob_adam_check_guards")
+    return bad.value
 
 
 def ob_adam_attach(cfg, workspace_ptr, ws_bytes, counters, stream_ptr):
@@ -275,6 +283,10 @@ class OneBitAdam:
         counters = ob_adam_get_counters(self.h)
         self.stream.synchronize()
         return self.workspace.to(device, copy=True), counters
+
+    def check_guards(self):
+        """-1 if no kernel wrote past a workspace buffer (synchronizes)."""
+        return ob_adam_check_guards(self.h)
 
     def params_view(self):
         """fp32[d] tensor aliasing the library's parameters x (no copy)."""

@@ -189,6 +189,17 @@ ob_status ob_adam_get_counters(ob_adam_t h, ob_adam_counters* out);
 ob_status ob_adam_attach(const ob_adam_config* cfg, void* workspace, uint64_t ws_bytes,
                          const ob_adam_counters* counters, void* stream, ob_adam_t* out);
 
+/* Workspace integrity check, for debugging and tests.  Every sub-buffer of
+ * the workspace is followed directly by a 256-byte guard region that
+ * ob_adam_init fills with a known pattern and no kernel writes.  This call
+ * synchronizes the handle's stream, reads the guards back and sets
+ * *first_bad to -1 when all are intact, else to the index (in workspace
+ * order: x, m, v, u, worker compensated slabs, worker sign words, server sign
+ * words, worker partials, server partials, fold buffer, worker scales, server
+ * scales) of the first guard found changed -- a write past that buffer's
+ * end.  A workspace adopted by ob_adam_attach keeps the guards of the copy. */
+ob_status ob_adam_check_guards(ob_adam_t h, int32_t* first_bad);
+
 /* Steps taken so far (warm-up and compressed) and compressed steps taken. */
 ob_status ob_adam_step_count(ob_adam_t h, int64_t* steps, int64_t* compressed_steps);
 

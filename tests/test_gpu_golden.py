@@ -142,4 +142,5 @@ def test_full_size_against_stored_oracle(name):
             check_sampled("%s chunk %d final e_w%d" % (name, j, i),
                           sampled(ob.OB_E_WORKER, rec, i), fin["e"][i])
         assert opt.steps[0] == rec["t"]
+    assert opt.check_guards() == -1, "a kernel wrote past the end of a workspace buffer"
     log("%s: %d chunks match the oracle at every step" % (name, len(recs)))

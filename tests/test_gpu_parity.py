@@ -84,6 +84,7 @@ def run_case(d, n, bf16, sigma, warm, comp, staged=False, exact=True, check_ever
         if staged_warm and t < warm:  # the partial sums were cleared from the error slabs
             for w in range(n):
                 assert not np.any(gpu_np(opt, ob.OB_E_WORKER, w)), "step %d e_w%d" % (t, w)
+    assert opt.check_guards() == -1, "a kernel wrote past the end of a workspace buffer"
     return opt, orc
 
 
@@ -316,3 +317,78 @@ def test_checkpoint_resume_is_bit_identical():
     for w in range(n):
         for f in (ob.OB_E_WORKER, ob.OB_BITS_WORKER, ob.OB_SCALE_WORKER):
             np.testing.assert_array_equal(gpu_np(a, f, w), gpu_np(b, f, w))
+
+
+def nan_aware_equal(what, got, want, exact):
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "%s: NaN positions differ" % what
+    if exact:
+        assert ulp_diff(got[~nan], want[~nan]) == 0, "%s: not bit-identical" % what
+    else:
+        from gpu_common import assert_close
+        assert_close(what, got[~nan], want[~nan])
+    return int(nan.sum())
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_nan_gradient_propagates_like_the_oracle(n):
+    """A NaN in one worker's gradient: its sign bit is 0 (NaN >= 0 is false),
+    its chunk's scale and everything derived from that chunk become NaN on
+    both sides, and every other chunk is untouched."""
+    import torch
+    d = n * 3392
+    opt = ob.OneBitAdam(d, n)
+    orc = oracle.Oracle(d, n)
+    L = d // n
+    k = 2 * L + 777  # chunk 2
+    for t in range(5):
+        hg = host_grads(d, n, t, sigma=1e-2)
+        if t == 2:
+            hg[1] = hg[1].copy()
+            hg[1][k] = np.float32(np.nan)
+        dg = [to_device_grad(g) for g in hg]
+        if t < 2:
+            opt.warmup_step(dg, np.float32(1e-3))
+            orc.warmup_step(hg, np.float32(1e-3))
+        else:
+            opt.compressed_step(dg, np.float32(1e-3))
+            orc.compressed_step(hg, np.float32(1e-3))
+        torch.cuda.synchronize()
+        if t < 2:
+            continue
+        for w in range(n):
+            np.testing.assert_array_equal(gpu_np(opt, ob.OB_BITS_WORKER, w),
+                                          orc.get(oracle.BITS_WORKER, w))
+            nan_aware_equal("step %d scales w%d" % (t, w), gpu_np(opt, ob.OB_SCALE_WORKER, w),
+                            orc.get(oracle.SCALE_WORKER, w), exact=True)
+            nan_aware_equal("step %d e_w%d" % (t, w), gpu_np(opt, ob.OB_E_WORKER, w),
+                            orc.get(oracle.E_WORKER, w), exact=True)
+        np.testing.assert_array_equal(gpu_np(opt, ob.OB_BITS_SERVER), orc.get(oracle.BITS_SERVER))
+        nan_aware_equal("step %d server scales" % t, gpu_np(opt, ob.OB_SCALE_SERVER),
+                        orc.get(oracle.SCALE_SERVER), exact=True)
+        for name, f, of in (("x", ob.OB_X, oracle.X), ("e_srv", ob.OB_E_SERVER, oracle.E_SERVER),
+                            ("m", ob.OB_M, oracle.M)):
+            cnt = nan_aware_equal("step %d %s" % (t, name), gpu_np(opt, f), orc.get(of), exact=True)
+            if name == "x":
+                assert cnt == L, "the whole of chunk 2 and nothing else is NaN"
+        assert (int(gpu_np(opt, ob.OB_BITS_WORKER, 1)[k // 64]) >> (k % 64)) & 1 == 0
+        assert np.isnan(gpu_np(opt, ob.OB_SCALE_WORKER, 1)[2])
+
+
+def test_guard_check_detects_a_write_past_a_buffer():
+    """The guards right after each workspace buffer: intact after steps, and
+    a byte changed (from the host) just past the parameters is reported as
+    guard 0; a restored copy carries its guards along."""
+    import torch
+    d, n = 4 * 3392, 4
+    opt = ob.OneBitAdam(d, n)
+    g = [to_device_grad(x) for x in host_grads(d, n, 0, sigma=1e-2)]
+    opt.warmup_step(g, 1e-3)
+    opt.compressed_step(g, 1e-3)
+    assert opt.check_guards() == -1
+    ck = opt.checkpoint()
+    assert ob.OneBitAdam(d, n, checkpoint=ck).check_guards() == -1
+    x_off = opt.params_view().data_ptr() - opt.workspace.data_ptr()
+    opt.workspace[x_off + 4 * d] ^= 0xFF  # first byte after x
+    torch.cuda.synchronize()
+    assert opt.check_guards() == 0
