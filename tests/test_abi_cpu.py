@@ -91,3 +91,17 @@ def test_attach_rejects_impossible_counters_without_gpu(ob):
     with pytest.raises(ob.ObAdamError) as e:
         ob.ob_adam_attach(cfg, 256, need - 1, (3, 1, 2), None)
     assert e.value.status == ob.OB_ERR_WORKSPACE
+
+
+def test_header_compiles_as_c99():
+    """The interface header is plain C: it compiles with gcc -std=c99
+    -pedantic and no warnings."""
+    import subprocess
+    import tempfile
+    src = '#include "ob_adam.h"\nint main(void) { ob_adam_config c = {0}; (void)c; return 0; }\n'
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "hdr.c")
+        with open(path, "w") as f:
+            f.write(src)
+        subprocess.check_call(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                               "-fsyntax-only", "-I", os.path.join(ROOT, "include"), path])
