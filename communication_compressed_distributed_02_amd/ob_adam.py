@@ -217,6 +217,11 @@ class OneBitAdam:
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         self.ws_bytes = ob_adam_workspace_bytes(self.cfg)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        # the library works on self.stream: tensors it touches are recorded
+        # on that stream so that torch does not hand their memory out again
+        # before the stream has passed, and each call is ordered after the
+        # caller's current stream (and the caller's stream after the call)
+        self._order_after_caller(self.workspace)
         if checkpoint is not None:
             data, counters = checkpoint
             if data.numel() != self.ws_bytes:
@@ -236,6 +241,19 @@ class OneBitAdam:
         self.h = ob_adam_init(self.cfg, self.workspace.data_ptr(), self.ws_bytes, x0p,
                               self.stream.cuda_stream)
 
+    def _separate(self):
+        return torch.cuda.current_stream(self.device) != self.stream
+
+    def _order_after_caller(self, *tensors):
+        if self._separate():
+            self.stream.wait_stream(torch.cuda.current_stream(self.device))
+            for t in tensors:
+                t.record_stream(self.stream)
+
+    def _order_caller_after(self):
+        if self._separate():
+            torch.cuda.current_stream(self.device).wait_stream(self.stream)
+
     def _grad_ptrs(self, grads):
         want = torch.bfloat16 if self.cfg.grad_dtype == OB_GRAD_BF16 else torch.float32
         ptrs = []
@@ -246,22 +264,38 @@ class OneBitAdam:
         return ptrs
 
     def warmup_step(self, grads, lr):
-        ob_adam_warmup_step(self.h, self._grad_ptrs(grads), lr)
+        ptrs = self._grad_ptrs(grads)
+        self._order_after_caller(*grads)
+        ob_adam_warmup_step(self.h, ptrs, lr)
+        self._order_caller_after()
 
     def warmup_worker(self, worker, grad):
-        ob_adam_warmup_worker(self.h, worker, self._grad_ptrs([grad])[0])
+        ptr = self._grad_ptrs([grad])[0]
+        self._order_after_caller(grad)
+        ob_adam_warmup_worker(self.h, worker, ptr)
+        self._order_caller_after()
 
     def warmup_finish(self, lr):
+        self._order_after_caller()
         ob_adam_warmup_finish(self.h, lr)
+        self._order_caller_after()
 
     def compressed_step(self, grads, lr):
-        ob_adam_compressed_step(self.h, self._grad_ptrs(grads), lr)
+        ptrs = self._grad_ptrs(grads)
+        self._order_after_caller(*grads)
+        ob_adam_compressed_step(self.h, ptrs, lr)
+        self._order_caller_after()
 
     def compress_worker(self, worker, grad):
-        ob_adam_compress_worker(self.h, worker, self._grad_ptrs([grad])[0])
+        ptr = self._grad_ptrs([grad])[0]
+        self._order_after_caller(grad)
+        ob_adam_compress_worker(self.h, worker, ptr)
+        self._order_caller_after()
 
     def compressed_finish(self, lr):
+        self._order_after_caller()
         ob_adam_compressed_finish(self.h, lr)
+        self._order_caller_after()
 
     def get(self, field, worker=0, offset=0, count=None):
         """Device tensor with `count` elements of a field (see include/ob_adam.h)."""
@@ -270,13 +304,17 @@ class OneBitAdam:
         if count is None:
             count = size - offset
         out = torch.empty(max(count, 0), dtype=_FIELD_DTYPE[field], device=self.device)
+        self._order_after_caller(out)
         ob_adam_get_state(self.h, field, worker, offset, count, out.data_ptr() if count else None)
+        self._order_caller_after()
         return out
 
     def set(self, field, src, offset=0):
         if src.dtype != torch.float32 or not src.is_contiguous():
             raise ValueError("source must be a contiguous float32 tensor")
+        self._order_after_caller(src)
         ob_adam_set_state(self.h, field, offset, src.numel(), src.data_ptr())
+        self._order_caller_after()
 
     def checkpoint(self, device="cpu"):
         """(copy of the workspace bytes, counters): the whole optimizer state."""

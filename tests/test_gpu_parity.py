@@ -409,3 +409,31 @@ def test_random_shapes_match_oracle():
         log("random shape %d: n=%d rows/chunk=%d bf16=%s staged=%s" % (case, n, rows, bf16, staged))
         run_case(d, n, bf16, 1e-3 if bf16 else 1e-2, 1 + case % 2, 2, staged=staged,
                  staged_warm=staged and case % 4 == 1)
+
+
+def test_library_on_its_own_stream():
+    """The handle on a stream of its own: gradients written on the caller's
+    stream right before each step, state read on the caller's stream right
+    after -- the binding orders the two streams, and every field matches the
+    oracle bit for bit."""
+    import torch
+    d, n = 8 * 3392, 8
+    side = torch.cuda.Stream()
+    opt = ob.OneBitAdam(d, n, stream=side)
+    orc = oracle.Oracle(d, n)
+    buf = [torch.empty(d, device="cuda") for _ in range(n)]
+    for t in range(5):
+        hg = host_grads(d, n, t, sigma=1e-2)
+        for w in range(n):  # on the caller's (current) stream
+            buf[w].copy_(torch.from_numpy(hg[w]).cuda(non_blocking=True))
+            buf[w].mul_(1.0)
+        if t < 2:
+            opt.warmup_step(buf, np.float32(1e-3))
+            orc.warmup_step(hg, np.float32(1e-3))
+        else:
+            opt.compressed_step(buf, np.float32(1e-3))
+            orc.compressed_step(hg, np.float32(1e-3))
+        x = opt.get(ob.OB_X)
+        assert ulp_diff(x.cpu().numpy(), orc.get(oracle.X)) == 0, "step %d x" % t
+    torch.cuda.synchronize()
+    compare_full(opt, orc, True, exact=True, where="own stream")
