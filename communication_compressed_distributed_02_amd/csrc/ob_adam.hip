@@ -35,13 +35,25 @@ namespace {
 
 bool valid_beta(float b) { return isfinite(b) && b >= 0.0f && b < 1.0f; }
 
+// 2^40 parameters: far beyond one GPU's memory, and small enough that no size
+// computed from d and n (at most 64 * 4 * d bytes) can overflow.
+constexpr int64_t kMaxParams = int64_t(1) << 40;
+
+bool aligned(const void* p, uintptr_t bytes) { return ((uintptr_t)p & (bytes - 1)) == 0; }
+
+// Gradient elements are read at their natural alignment.
+bool grad_aligned(const ob_adam_t h, const void* g) {
+  return aligned(g, h->st.grad_bf16 ? 2 : 4);
+}
+
 ob_status check_config(const ob_adam_config* cfg) {
   if (cfg == nullptr) return OB_ERR_ARG;
   if (cfg->grad_dtype != OB_GRAD_F32 && cfg->grad_dtype != OB_GRAD_BF16) return OB_ERR_ARG;
   if (!valid_beta(cfg->beta1) || !valid_beta(cfg->beta2) || !isfinite(cfg->eps) ||
       cfg->eps < 0.0f)
     return OB_ERR_ARG;
-  if (cfg->d <= 0 || cfg->n_workers < 1 || cfg->n_workers > ob::kMaxWorkersPerLaunch)
+  if (cfg->d <= 0 || cfg->d > kMaxParams || cfg->n_workers < 1 ||
+      cfg->n_workers > ob::kMaxWorkersPerLaunch)
     return OB_ERR_SHAPE;
   if (cfg->d % (64 * (int64_t)cfg->n_workers) != 0) return OB_ERR_SHAPE;
   const int64_t L = cfg->d / cfg->n_workers;
@@ -92,7 +104,7 @@ void release_events(ob_adam_t h) {
 ob_status gather_grads(ob_adam_t h, const void* const* grads, int w0, int nw, ob::GradPtrs* g) {
   if (grads == nullptr) return OB_ERR_ARG;
   for (int i = 0; i < nw; ++i) {
-    if (grads[w0 + i] == nullptr) return OB_ERR_ARG;
+    if (grads[w0 + i] == nullptr || !grad_aligned(h, grads[w0 + i])) return OB_ERR_ARG;
     g->p[i] = grads[w0 + i];
   }
   (void)h;
@@ -268,7 +280,8 @@ ob_status ob_adam_warmup_step(ob_adam_t h, const void* const* grads, float lr) {
 ob_status ob_adam_warmup_worker(ob_adam_t h, int32_t worker, const void* grad) {
   ob_status st = usable(h);
   if (st != OB_OK) return st;
-  if (worker < 0 || worker >= h->st.n || grad == nullptr) return OB_ERR_ARG;
+  if (worker < 0 || worker >= h->st.n || grad == nullptr || !grad_aligned(h, grad))
+    return OB_ERR_ARG;
   if (h->compressed > 0 || h->staged_open) return OB_ERR_PHASE;
   if (worker != (h->warm_open ? h->warm_next : 0)) return OB_ERR_PHASE;
   st = fail(h, timed(h, OB_K_WARMUP, [&](hipEvent_t a, hipEvent_t b) {
@@ -316,7 +329,8 @@ ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float l
 ob_status ob_adam_compress_worker(ob_adam_t h, int32_t worker, const void* grad) {
   ob_status st = usable(h);
   if (st != OB_OK) return st;
-  if (worker < 0 || worker >= h->st.n || grad == nullptr) return OB_ERR_ARG;
+  if (worker < 0 || worker >= h->st.n || grad == nullptr || !grad_aligned(h, grad))
+    return OB_ERR_ARG;
   if (h->warm == 0 || h->warm_open) return OB_ERR_PHASE;
   const uint64_t bit = (uint64_t)1 << worker;
   if (h->staged_open && (h->staged_mask & bit)) return OB_ERR_PHASE;
@@ -368,6 +382,8 @@ ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t 
   if (offset < 0 || count < 0 || offset > size || count > size - offset) return OB_ERR_ARG;
   if (count == 0) return OB_OK;
   if (dst_device == nullptr) return OB_ERR_ARG;
+  const bool words = field == OB_BITS_WORKER || field == OB_BITS_SERVER;
+  if (!aligned(dst_device, words ? 8 : 4)) return OB_ERR_ARG;
   hipError_t e = hipSuccess;
   auto copy = [&](const void* src, size_t elem) {
     return hipMemcpyAsync(dst_device, (const char*)src + elem * (size_t)offset,
@@ -415,7 +431,7 @@ ob_status ob_adam_set_state(ob_adam_t h, int32_t field, int64_t offset, int64_t 
   }
   if (offset < 0 || count < 0 || offset > s.d || count > s.d - offset) return OB_ERR_ARG;
   if (count == 0) return OB_OK;
-  if (src_device == nullptr) return OB_ERR_ARG;
+  if (src_device == nullptr || !aligned(src_device, 4)) return OB_ERR_ARG;
   return fail(h, hipMemcpyAsync(dst + offset, src_device, sizeof(float) * (size_t)count,
                                 hipMemcpyDeviceToDevice, h->stream));
 }
@@ -502,7 +518,8 @@ const char* ob_status_str(ob_status s) {
   switch (s) {
     case OB_OK: return "ok";
     case OB_ERR_ARG: return "invalid argument";
-    case OB_ERR_SHAPE: return "unsupported shape (need d > 0, 1 <= n <= 64, d % (64*n) == 0)";
+    case OB_ERR_SHAPE:
+      return "unsupported shape (need 0 < d <= 2^40, 1 <= n <= 64, d % (64*n) == 0, d/n <= 2^31)";
     case OB_ERR_PHASE: return "call out of order for the current phase";
     case OB_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case OB_ERR_HIP: return "HIP runtime error (handle poisoned)";

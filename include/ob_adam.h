@@ -44,6 +44,10 @@
  * owns only the host handle.  The workspace must stay valid until
  * ob_adam_destroy.  A handle is not thread-safe.
  *
+ * Alignment: gradients are aligned to their element size (4 bytes fp32, 2
+ * bytes bf16), get/set buffers to the field's element size (8 bytes for sign
+ * words, else 4); OB_ERR_ARG otherwise.
+ *
  * Streams: every call is enqueued on the stream given to ob_adam_init (a
  * hipStream_t passed as void*; NULL = the null stream) and returns without
  * waiting, except where stated.  Gradients must stay valid until the stream
@@ -69,7 +73,7 @@ typedef struct ob_adam_handle* ob_adam_t;
 
 typedef enum {
   OB_OK = 0,
-  OB_ERR_ARG = 1,       /* null pointer, bad dtype, bad worker index, bad range */
+  OB_ERR_ARG = 1,       /* null or misaligned pointer, bad dtype, bad worker index, bad range */
   OB_ERR_SHAPE = 2,     /* d, n do not satisfy the shape rule */
   OB_ERR_PHASE = 3,     /* call out of order (see each entry point) */
   OB_ERR_WORKSPACE = 4, /* workspace too small or misaligned */
@@ -80,7 +84,8 @@ typedef enum {
 enum { OB_GRAD_F32 = 0, OB_GRAD_BF16 = 1 };
 
 typedef struct {
-  int64_t d;          /* parameters; d > 0 and d % (64*n_workers) == 0 */
+  int64_t d;          /* parameters; 0 < d <= 2^40, d % (64*n_workers) == 0 and
+                         d / n_workers <= 2^31 (chunk length) */
   int32_t n_workers;  /* simulated workers; 1 <= n_workers <= 64 */
   int32_t grad_dtype; /* OB_GRAD_F32 or OB_GRAD_BF16 (bf16 is widened exactly) */
   float beta1, beta2, eps;

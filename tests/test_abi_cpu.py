@@ -45,7 +45,10 @@ def test_workspace_bytes_and_shape_rules(ob):
     b = ob.ob_adam_workspace_bytes(ob.make_config(1 << 20, 4))
     # x, m, v, u + 4 compensated slabs, dominant terms
     assert b >= 8 * 4 * (1 << 20)
-    for d, n in ((1000, 4), (64 * 4 + 64, 4), (0, 1), (64 * 65, 65), (64, 0)):
+    # the largest shapes accepted: chunks of 2^31 elements (64 workers: d = 2^37)
+    assert ob.ob_adam_workspace_bytes(ob.make_config(1 << 37, 64)) > 64 * 4 * (1 << 37)
+    for d, n in ((1000, 4), (64 * 4 + 64, 4), (0, 1), (64 * 65, 65), (64, 0), (-64, 1),
+                 ((1 << 31) + 64, 1), ((1 << 37) + 64 * 64, 64), ((1 << 40) + 64, 64)):
         with pytest.raises(ob.ObAdamError) as e:
             ob.ob_adam_workspace_bytes(ob.make_config(d, n))
         assert e.value.status == ob.OB_ERR_SHAPE

@@ -275,6 +275,19 @@ def test_phase_rules_and_ranges():
     with pytest.raises(ob.ObAdamError) as e:
         opt.compress_worker(n, g[0])
     assert e.value.status == ob.OB_ERR_ARG
+    # misaligned pointers are argument errors, checked before anything is enqueued
+    raw = torch.zeros(d + 1, device="cuda")
+    odd = raw[1:]  # 4-byte but not 8-byte aligned
+    with pytest.raises(ob.ObAdamError) as e:
+        ob.ob_adam_compressed_step(opt.h, [odd.data_ptr() + 2] + [x.data_ptr() for x in g[1:]],
+                                   1e-3)
+    assert e.value.status == ob.OB_ERR_ARG
+    with pytest.raises(ob.ObAdamError) as e:
+        ob.ob_adam_get_state(opt.h, ob.OB_BITS_SERVER, 0, 0, 4, odd.data_ptr())
+    assert e.value.status == ob.OB_ERR_ARG
+    with pytest.raises(ob.ObAdamError) as e:
+        ob.ob_adam_set_state(opt.h, ob.OB_X, 0, 4, raw.data_ptr() + 1)
+    assert e.value.status == ob.OB_ERR_ARG
     # errors leave the state untouched: the step still runs and counts
     opt.compressed_step(g, 1e-3)
     assert opt.steps == (3, 2)
