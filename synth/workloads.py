@@ -129,10 +129,16 @@ def make(name):
         d, pads, raw = _flat(340_000_000, 64)
         return Workload("c5", d=d, n=64, warmup=30, compressed=170, sigma=1e-3,
                         linear_decay=True, staged=True, pads=pads, raw=raw)
+    if name == "idx64":
+        # not a workload of the pages: the largest arrays of the tests, so
+        # that element indices run past 2^31 (chunk 3 straddles it)
+        d = (1 << 31) + (1 << 22)
+        return Workload("idx64", d=d, n=4, warmup=1, compressed=2, sigma=1e-3, bf16=True, raw=d)
     raise KeyError(name)
 
 
 NAMES = ("c1", "c2", "c3", "c4", "c5")
+EXTRA = ("idx64",)  # size edge case of the tests
 
 
 def describe(w):

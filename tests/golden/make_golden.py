@@ -28,16 +28,23 @@ import oracle  # noqa: E402
 from synth import workloads as W  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SAMPLED = {"c1": [0, 1, 2, 3], "c2": list(range(8)), "c3": list(range(16)), "c4": [0, 7],
-           "c5": [0, 31, 63]}
+SAMPLED = {"c1": [0, 1, 2, 3], "c2": list(range(8)), "c3": list(range(16)), "c4": [0, 3, 5, 7],
+           "c5": [0, 15, 31, 47, 63], "idx64": [3]}
 N_SAMPLES = 256
 
 
 def sample_indices(w, j):
-    """Sorted global indices of the sampled elements of chunk j (first and last included)."""
+    """Sorted global indices of the sampled elements of chunk j (first and last
+    included; for a chunk that holds element 2^31, also the elements around it
+    and 60 past it)."""
     rng = np.random.default_rng(1000 + j)
     loc = rng.choice(w.L, N_SAMPLES, replace=False)
     loc[0], loc[1] = 0, w.L - 1
+    b = (1 << 31) - j * w.L
+    if 2 <= b < w.L - 2:
+        extra = np.concatenate([np.arange(b - 2, b + 2),
+                                b + rng.choice(w.L - b, 60, replace=False)])
+        loc = np.unique(np.concatenate([loc, extra]))
     loc.sort()
     return j * w.L + loc
 

@@ -1,4 +1,5 @@
-"""Parity at the full sizes of the four large workloads, in the launch
+"""Parity at the full sizes of the four large workloads (and of idx64, whose
+element indices run past 2^31), in the launch
 configuration bench.py times, against values the CPU oracle stored
 (tests/golden/<workload>/chunk_<j>.json, written by make_golden.py from the
 oracle and the seeded input generator only).
@@ -45,7 +46,7 @@ def check_sampled(what, got, want_bits):
                              % (what, int((~ok).sum()), ok.size, got[i], want[i]))
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "idx64"])
 def test_full_size_against_stored_oracle(name):
     import torch
 
