@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include <new>
 #include <vector>
@@ -25,6 +27,7 @@ struct ob_adam_handle {
   bool warm_open;       // a worker-at-a-time warm-up step has started
   int warm_next;        // the next worker that step expects
   bool poisoned;
+  int32_t debug = 0;    // OB_DEBUG_* flags
   // per-kernel timing (events recorded around each launch when enabled)
   std::vector<hipEvent_t> ev;          // 2 per timed launch
   std::vector<int> ev_kernel;          // kernel id of each timed launch
@@ -76,7 +79,7 @@ ob_status usable(ob_adam_t h) {
 // Run launcher `fn(t0, t1)`, handing it a pair of timing events when timing
 // is on (the events are taken from the dispatch packets themselves).
 template <typename F>
-hipError_t timed(ob_adam_t h, int kernel, F fn) {
+hipError_t timed_launch(ob_adam_t h, int kernel, F fn) {
   const int64_t cap = (int64_t)h->ev_kernel.size();
   if (cap == 0) return fn(nullptr, nullptr);
   if (h->ev_used >= cap) {
@@ -89,6 +92,54 @@ hipError_t timed(ob_adam_t h, int kernel, F fn) {
   h->ev_kernel[i] = kernel;
   h->ev_used = i + 1;
   return hipSuccess;
+}
+
+// The launch, then (debug mode) a wait for it, so that an error is reported
+// by the call that launched the failing kernel.
+template <typename F>
+hipError_t timed(ob_adam_t h, int kernel, F fn) {
+  hipError_t e = timed_launch(h, kernel, fn);
+  if (e == hipSuccess && (h->debug & OB_DEBUG_SYNC)) {
+    e = hipStreamSynchronize(h->stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess)
+      fprintf(stderr, "ob_adam: kernel %d (OB_K_*) failed: %s\n", kernel, hipGetErrorString(e));
+  }
+  return e;
+}
+
+// Synchronize and compare every guard with its pattern; *first_bad = -1 if
+// all are intact, else the first changed one.
+hipError_t read_guards(ob_adam_t h, int32_t* first_bad) {
+  hipError_t e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) return e;
+  uint32_t words[ob::kGuardBytes / 4];
+  *first_bad = -1;
+  for (int i = 0; i < ob::kNumGuards; ++i) {
+    e = hipMemcpy(words, h->base + h->layout.guard[i], ob::kGuardBytes, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    for (uint64_t k = 0; k < ob::kGuardBytes / 4; ++k) {
+      if (words[k] != ob::guard_word(i)) {
+        *first_bad = i;
+        return hipSuccess;
+      }
+    }
+  }
+  return hipSuccess;
+}
+
+// After a completed step (debug mode): the workspace guards must be intact.
+ob_status after_step(ob_adam_t h) {
+  if (!(h->debug & OB_DEBUG_GUARDS)) return OB_OK;
+  int32_t bad = -1;
+  if (read_guards(h, &bad) != hipSuccess) return fail(h, hipErrorUnknown);
+  if (bad >= 0) {
+    fprintf(stderr, "ob_adam: workspace guard %d changed by step %lld\n", bad,
+            (long long)h->steps);
+    h->poisoned = true;
+    return OB_ERR_HIP;
+  }
+  return OB_OK;
 }
 
 void release_events(ob_adam_t h) {
@@ -143,7 +194,7 @@ ob_status finish_step(ob_adam_t h, float lr) {
   if (e != hipSuccess) return fail(h, e);
   h->steps += 1;
   h->compressed += 1;
-  return OB_OK;
+  return after_step(h);
 }
 
 }  // namespace
@@ -191,6 +242,8 @@ ob_adam_handle* make_handle(const ob_adam_config* cfg, void* workspace, void* st
   s.wscale = (float*)(base + l.wscale);
   s.sscale = (float*)(base + l.sscale);
   h->stream = (hipStream_t)stream;
+  const char* dbg = getenv("OB_DEBUG");
+  if (dbg != nullptr) h->debug = atoi(dbg) & (OB_DEBUG_SYNC | OB_DEBUG_GUARDS);
   return h;
 }
 
@@ -274,7 +327,7 @@ ob_status ob_adam_warmup_step(ob_adam_t h, const void* const* grads, float lr) {
   if (st != OB_OK) return st;
   h->steps = t;
   h->warm += 1;
-  return OB_OK;
+  return after_step(h);
 }
 
 ob_status ob_adam_warmup_worker(ob_adam_t h, int32_t worker, const void* grad) {
@@ -308,7 +361,7 @@ ob_status ob_adam_warmup_finish(ob_adam_t h, float lr) {
   h->warm_next = 0;
   h->steps = t;
   h->warm += 1;
-  return OB_OK;
+  return after_step(h);
 }
 
 ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float lr) {
@@ -351,11 +404,10 @@ ob_status ob_adam_compressed_finish(ob_adam_t h, float lr) {
   if (st != OB_OK) return st;
   const uint64_t all = h->st.n == 64 ? ~(uint64_t)0 : (((uint64_t)1 << h->st.n) - 1);
   if (!h->staged_open || h->staged_mask != all) return OB_ERR_PHASE;
-  st = finish_step(h, lr);
-  if (st != OB_OK) return st;
+  st = finish_step(h, lr);  // errors here leave the handle poisoned
   h->staged_open = false;
   h->staged_mask = 0;
-  return OB_OK;
+  return st;
 }
 
 ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t offset,
@@ -439,20 +491,13 @@ ob_status ob_adam_set_state(ob_adam_t h, int32_t field, int64_t offset, int64_t 
 ob_status ob_adam_check_guards(ob_adam_t h, int32_t* first_bad) {
   if (h == nullptr || first_bad == nullptr) return OB_ERR_ARG;
   if (h->poisoned) return OB_ERR_HIP;
-  if (hipStreamSynchronize(h->stream) != hipSuccess) return fail(h, hipErrorUnknown);
-  uint32_t words[ob::kGuardBytes / 4];
-  *first_bad = -1;
-  for (int i = 0; i < ob::kNumGuards; ++i) {
-    if (hipMemcpy(words, h->base + h->layout.guard[i], ob::kGuardBytes,
-                  hipMemcpyDeviceToHost) != hipSuccess)
-      return fail(h, hipErrorUnknown);
-    for (uint64_t k = 0; k < ob::kGuardBytes / 4; ++k) {
-      if (words[k] != ob::guard_word(i)) {
-        *first_bad = i;
-        return OB_OK;
-      }
-    }
-  }
+  if (read_guards(h, first_bad) != hipSuccess) return fail(h, hipErrorUnknown);
+  return OB_OK;
+}
+
+ob_status ob_adam_set_debug(ob_adam_t h, int32_t flags) {
+  if (h == nullptr || (flags & ~(OB_DEBUG_SYNC | OB_DEBUG_GUARDS)) != 0) return OB_ERR_ARG;
+  h->debug = flags;
   return OB_OK;
 }
 

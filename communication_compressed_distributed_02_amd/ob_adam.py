@@ -23,7 +23,8 @@ EXPORTED = ("ob_adam_workspace_bytes", "ob_adam_init", "ob_adam_warmup_step",
             "ob_adam_warmup_worker", "ob_adam_warmup_finish",
             "ob_adam_compressed_step", "ob_adam_compress_worker", "ob_adam_compressed_finish",
             "ob_adam_get_state", "ob_adam_set_state", "ob_adam_params", "ob_adam_step_count",
-            "ob_adam_get_counters", "ob_adam_attach", "ob_adam_check_guards", "ob_adam_set_timing",
+            "ob_adam_get_counters", "ob_adam_attach", "ob_adam_check_guards", "ob_adam_set_debug",
+            "ob_adam_set_timing",
             "ob_adam_kernel_times", "ob_adam_destroy", "ob_status_str")
 KERNELS = ("warmup", "worker", "worker_scale", "server", "server_scale", "update")
 
@@ -66,6 +67,7 @@ def _load(path=LIB_PATH):
         "ob_adam_get_counters": [P, ctypes.POINTER(ob_adam_counters)],
         "ob_adam_attach": [cfgp, P, U64, ctypes.POINTER(ob_adam_counters), P, ctypes.POINTER(P)],
         "ob_adam_check_guards": [P, ctypes.POINTER(I32)],
+        "ob_adam_set_debug": [P, I32],
         "ob_adam_step_count": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "ob_adam_set_timing": [P, I32],
         "ob_adam_kernel_times": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64),
@@ -164,6 +166,13 @@ def ob_adam_check_guards(h):
     bad = ctypes.c_int32(0)
     _check(_lib.ob_adam_check_guards(h, ctypes.byref(bad)), "ob_adam_check_guards")
     return bad.value
+
+
+OB_DEBUG_SYNC, OB_DEBUG_GUARDS = 1, 2
+
+
+def ob_adam_set_debug(h, flags):
+    _check(_lib.ob_adam_set_debug(h, flags), "ob_adam_set_debug")
 
 
 def ob_adam_attach(cfg, workspace_ptr, ws_bytes, counters, stream_ptr):

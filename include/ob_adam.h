@@ -205,6 +205,19 @@ ob_status ob_adam_attach(const ob_adam_config* cfg, void* workspace, uint64_t ws
  * end.  A workspace adopted by ob_adam_attach keeps the guards of the copy. */
 ob_status ob_adam_check_guards(ob_adam_t h, int32_t* first_bad);
 
+/* Debug mode (off by default; also set at init from the environment variable
+ * OB_DEBUG, read as an integer of these flags):
+ *  OB_DEBUG_SYNC   - every kernel launch is followed by a wait for the
+ *                    stream, so that a failing kernel is reported (on stderr,
+ *                    with its OB_K_* id) by the call that launched it;
+ *  OB_DEBUG_GUARDS - after every completed step the workspace guards are
+ *                    checked; a changed guard is reported on stderr, the
+ *                    handle is poisoned and the step returns OB_ERR_HIP.
+ * Both make every call synchronous; the results are unchanged.  OB_ERR_ARG
+ * for other flag bits. */
+enum { OB_DEBUG_SYNC = 1, OB_DEBUG_GUARDS = 2 };
+ob_status ob_adam_set_debug(ob_adam_t h, int32_t flags);
+
 /* Steps taken so far (warm-up and compressed) and compressed steps taken. */
 ob_status ob_adam_step_count(ob_adam_t h, int64_t* steps, int64_t* compressed_steps);
 

@@ -72,6 +72,9 @@ def test_null_handle_is_an_argument_error(ob):
         ob.ob_adam_compressed_finish(None, 1e-3)
     assert e.value.status == ob.OB_ERR_ARG
     assert ob.ob_status_str(ob.OB_ERR_PHASE).startswith("call out of order")
+    with pytest.raises(ob.ObAdamError) as e:
+        ob.ob_adam_set_debug(None, ob.OB_DEBUG_SYNC)
+    assert e.value.status == ob.OB_ERR_ARG
 
 
 def test_front_end_flat_layout(ob):

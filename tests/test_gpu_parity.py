@@ -450,3 +450,37 @@ def test_library_on_its_own_stream():
         assert ulp_diff(x.cpu().numpy(), orc.get(oracle.X)) == 0, "step %d x" % t
     torch.cuda.synchronize()
     compare_full(opt, orc, True, exact=True, where="own stream")
+
+
+def test_debug_mode_same_results_and_reports_a_changed_guard():
+    """Debug mode (wait after every kernel, guards checked after every step),
+    set by the call or by OB_DEBUG at init: the same bits as without it; a
+    guard changed from the host makes the next step fail and poisons the
+    handle."""
+    import os
+    import torch
+    d, n = 8 * 3392, 8
+    plain, _ = run_case(d, n, True, 1e-3, 2, 3, check_every=False)
+    os.environ["OB_DEBUG"] = "3"
+    try:
+        dbg = ob.OneBitAdam(d, n, ob.OB_GRAD_BF16)
+    finally:
+        del os.environ["OB_DEBUG"]
+    for t in range(5):
+        g = [to_device_grad(x) for x in host_grads(d, n, t, sigma=1e-3, bf16=True)]
+        (dbg.warmup_step if t < 2 else dbg.compressed_step)(g, np.float32(1e-3))
+    for f in (ob.OB_X, ob.OB_E_SERVER, ob.OB_BITS_SERVER):
+        np.testing.assert_array_equal(gpu_np(dbg, f), gpu_np(plain, f))
+    other = ob.OneBitAdam(4 * 3392, 4)
+    ob.ob_adam_set_debug(other.h, ob.OB_DEBUG_SYNC | ob.OB_DEBUG_GUARDS)
+    g = [to_device_grad(x) for x in host_grads(4 * 3392, 4, 0, sigma=1e-2)]
+    other.warmup_step(g, 1e-3)
+    x_off = other.params_view().data_ptr() - other.workspace.data_ptr()
+    other.workspace[x_off + 4 * 4 * 3392 + 8] ^= 0x1
+    torch.cuda.synchronize()
+    with pytest.raises(ob.ObAdamError) as e:
+        other.compressed_step(g, 1e-3)
+    assert e.value.status == ob.OB_ERR_HIP
+    with pytest.raises(ob.ObAdamError) as e:  # poisoned
+        other.compressed_step(g, 1e-3)
+    assert e.value.status == ob.OB_ERR_HIP
