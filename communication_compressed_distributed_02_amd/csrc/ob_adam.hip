@@ -15,19 +15,19 @@
 #include "ob_kernels.h"
 
 struct ob_adam_handle {
-  ob::State st;
-  char* base;           // the caller's workspace
-  ob::Layout layout;
-  hipStream_t stream;
-  int64_t steps;        // warm-up + compressed steps taken
-  int64_t compressed;   // compressed steps taken
-  int64_t warm;         // warm-up steps taken
-  bool staged_open;     // a worker-at-a-time step has started
-  uint64_t staged_mask; // workers already compressed in the open step
-  bool warm_open;       // a worker-at-a-time warm-up step has started
-  int warm_next;        // the next worker that step expects
-  bool poisoned;
-  int32_t debug = 0;    // OB_DEBUG_* flags
+  ob::State st{};
+  char* base = nullptr;       // the caller's workspace
+  ob::Layout layout{};
+  hipStream_t stream = nullptr;
+  int64_t steps = 0;          // warm-up + compressed steps taken
+  int64_t compressed = 0;     // compressed steps taken
+  int64_t warm = 0;           // warm-up steps taken
+  bool staged_open = false;   // a worker-at-a-time step has started
+  uint64_t staged_mask = 0;   // workers already compressed in the open step
+  bool warm_open = false;     // a worker-at-a-time warm-up step has started
+  int warm_next = 0;          // the next worker that step expects
+  bool poisoned = false;
+  int32_t debug = 0;          // OB_DEBUG_* flags
   // per-kernel timing (events recorded around each launch when enabled)
   std::vector<hipEvent_t> ev;          // 2 per timed launch
   std::vector<int> ev_kernel;          // kernel id of each timed launch
@@ -158,7 +158,6 @@ ob_status gather_grads(ob_adam_t h, const void* const* grads, int w0, int nw, ob
     if (grads[w0 + i] == nullptr || !grad_aligned(h, grads[w0 + i])) return OB_ERR_ARG;
     g->p[i] = grads[w0 + i];
   }
-  (void)h;
   return OB_OK;
 }
 
