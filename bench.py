@@ -9,9 +9,14 @@ sized flat vector), n = 8 simulated workers, bf16 gradients N(0, 1e-3),
 2 full-precision warm-up steps before the compressed ones.  All gradient
 batches are generated on the GPU before the timed region.
 
-Prints one JSON line: params*workers/s of the whole step, the worker pass's
-roofline against MI355X's 8 TB/s HBM peak (timed live with HIP events the
-library records on its stream), and the CPU oracle timed on a bounded sample.
+Prints one JSON line with:
+- params*workers/s of the whole step;
+- the worker pass's roofline against MI355X's 8 TB/s HBM peak, timed live
+  with HIP events the library records on its stream, plus the profiler's
+  byte counters when they were taken on the current kernel code;
+- the step's other kernels and streaming probes of the same access mix;
+- the CPU oracle timed on a bounded sample (chunk 0), and the comparison of
+  its state with the GPU's after the same steps (parity).
 """
 import argparse
 import hashlib
