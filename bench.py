@@ -241,7 +241,8 @@ def stream_ceilings(n, bf16=True, reps=5):
     """GB/s of the probes over n elements on this device: the worker pass's
     access mix (bf16 gradients: 6 B read + 4 B written per element; fp32:
     8 + 4), copy, read-only and write-only, with the step's own wave-row
-    mapping and non-temporal hints."""
+    mapping and non-temporal hints; and, for reference, the same mix as a
+    torch elementwise kernel and a runtime device-to-device copy."""
     import torch
     lib = probe_lib()
     n -= n % 4096
@@ -263,6 +264,22 @@ def stream_ceilings(n, bf16=True, reps=5):
         torch.cuda.synchronize()
         out[("mix" if kind == "mix32" else kind) + "_GB_s"] = round(
             nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    # the same access mix and a copy as the vendor stack implements them:
+    # torch's elementwise c += g (the gradient widened to fp32 on the fly),
+    # and the runtime's device-to-device copy
+    gt = g.view(torch.bfloat16) if bf16 else g
+    for name, fn, nbytes in (("torch_mix", lambda: c.add_(gt), (6 if bf16 else 8) * n + 4 * n),
+                             ("runtime_copy", lambda: c2.copy_(c), 8 * n)):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_GB_s"] = round(nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     del g, c, c2
     torch.cuda.empty_cache()
     return out
@@ -435,8 +452,9 @@ def main():
     torch.cuda.empty_cache()
     ceil = stream_ceilings(min(w.n * w.d if not w.staged else w.d, 1 << 31), w.bf16)
     ceil["note"] = ("probe kernels with the worker pass's mapping over as many elements as one "
-                    "launch of it (at most 2^31); mix = its %d B read + 4 B written per element"
-                    % (6 if w.bf16 else 8))
+                    "launch of it (at most 2^31); mix = its %d B read + 4 B written per element; "
+                    "torch_mix = the same mix as torch's c += g, runtime_copy = a device-to-"
+                    "device copy" % (6 if w.bf16 else 8))
     ceil["worker_frac_of_mix"] = round(wk["GB_s"] / ceil["mix_GB_s"], 4)
     result["ceilings"] = ceil
     if not a.no_cpu_baseline:
