@@ -137,7 +137,13 @@ ob_status ob_adam_warmup_finish(ob_adam_t h, float lr);
 /* One compression-phase step (the contract above), all n workers at once.
  * grads as for ob_adam_warmup_step.  OB_ERR_PHASE before any warm-up step or
  * while a staged step is open.  The variance is the one left by the last
- * warm-up step and is never written again. */
+ * warm-up step and is never written again.
+ * The call enqueues kernel launches only (no allocation, no memset, no wait
+ * for the stream unless debug mode is on), so a caller may capture it in a
+ * HIP graph on the handle's stream, after the first compressed step (which
+ * reads the warm-up's fp32 momentum); each replay is one more step with the
+ * captured gradients' addresses and lr.  The step counters count calls, so
+ * replays are not counted. */
 ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float lr);
 
 /* The same step with the gradients supplied one worker at a time, so that a
