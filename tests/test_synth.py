@@ -50,3 +50,30 @@ def test_bf16_round_to_nearest_even():
     for nb in (b - 1, b + 1):
         other = (nb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         assert np.all(err <= np.abs(other - f))
+
+
+def test_workloads_have_the_stated_shapes():
+    """The five workloads' padded sizes, worker counts, tensor counts, step
+    splits and c5's learning-rate decay, as the workload list states them
+    (architecture shapes of BERT-Base/Large and GPT-2-XL; 15 % of 200 steps
+    of warm-up for c5)."""
+    import numpy as np
+    from synth import workloads as W
+    want = {  # d, n, tensors, raw elements, warm-up, compressed, bf16, staged
+        "c1": (1 << 20, 4, 1, 1 << 20, 3, 7, False, False),
+        "c2": (110_000_128, 8, 1, 110_000_000, 2, 20, True, False),
+        "c3": (334_123_008, 16, 390, 334_122_810, 3, 7, False, False),
+        "c4": (1_557_611_520, 8, 580, 1_557_611_200, 3, 50, False, False),
+        "c5": (340_000_768, 64, 1, 340_000_000, 30, 170, False, True),
+    }
+    for name, (d, n, tensors, raw, warm, comp, bf16, staged) in want.items():
+        w = W.make(name)
+        assert (w.d, w.n, w.tensors, w.raw, w.warmup, w.compressed, w.bf16, w.staged) == \
+            (d, n, tensors, raw, warm, comp, bf16, staged), name
+        assert w.d % (64 * w.n) == 0, name
+        # the padding ranges cover exactly d - raw elements
+        assert sum(b - a for a, b in w.pads) == w.d - w.raw, name
+    c5 = W.make("c5")
+    assert c5.lr_at(29) == np.float32(1e-3) and c5.lr_at(30) == np.float32(1e-3)
+    assert c5.lr_at(199) == np.float32(1e-3 / 170)
+    assert W.make("c4").dist == W.STUDENT_T3
