@@ -28,7 +28,7 @@ import oracle  # noqa: E402
 from synth import workloads as W  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SAMPLED = {"c1": [0, 1, 2, 3], "c2": list(range(8)), "c3": list(range(16)), "c4": [0, 2, 3, 5, 6, 7],
+SAMPLED = {"c1": [0, 1, 2, 3], "c2": list(range(8)), "c3": list(range(16)), "c4": list(range(8)),
            "c5": [0, 15, 31, 47, 63], "idx64": [3]}
 N_SAMPLES = 256
 
