@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "compressed-step params·workers/sec and achieved HBM GB/s (% of peak), 1 GPU"
 KERNEL_SRC = os.path.join(ROOT, "communication_compressed_distributed_02_amd", "csrc",
                           "ob_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "worker_pass_c2_counters.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "worker_pass_%s_counters.txt")  # % workload
 
 
 def alg_bytes(w):
@@ -82,7 +82,7 @@ def load_traffic(workload):
     on the current kernel source (else None)."""
     t = None
     try:
-        for line in open(TRAFFIC_FILE):
+        for line in open(TRAFFIC_FILE % workload):
             if line.startswith("traffic_record: "):
                 t = json.loads(line[len("traffic_record: "):])
     except (OSError, ValueError):
