@@ -1,7 +1,7 @@
 """The pins must catch plausible mistakes: each mutant below is the oracle
 with one deliberate error (a dropped term, a wrong sign, a transposed index,
-a misplaced feedback), built on the CPU into a temporary library; the pin
-suite run against it has to fail."""
+a misplaced feedback), built on the CPU into a temporary library; the pins
+and the exact-arithmetic brute force run against it have to fail."""
 import os
 import subprocess
 import sys
@@ -51,6 +51,7 @@ def test_pins_catch_mutant(name):
                                "-o", so, c, "-lm"])
         env = dict(os.environ, OB_ORACLE_LIB=so)
         r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                            os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                            os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                            os.path.join(ROOT, "tests", "test_oracle_bruteforce.py")],
                            cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
         assert r.returncode != 0, "pins did not catch mutant %s:\n%s" % (name, r.stdout[-2000:])
