@@ -47,9 +47,13 @@ def alg_bytes(w):
     nseg = -(-w.L // 1024)
     part_w = 8 * n * n * nseg
     part_s = 8 * n * nseg
+    # worker-pass launches per step: one for all workers, or one per worker
+    # when the gradients come one worker at a time (each launch reads the
+    # momentum's sign words)
+    launches = n if w.staged else 1
     return {
         # grad in, compensated momentum in and out, sign words out, momentum words in
-        "worker": n * d * (gb + 4 + 4) + n * d // 8 + d // 8 + part_w,
+        "worker": n * d * (gb + 4 + 4) + n * d // 8 + launches * (d // 8) + part_w,
         "worker_scale": part_w + 4 * n * n,
         # worker sign words in, server u in and out, server words out
         "server": n * d // 8 + 8 * d + d // 8 + part_s + 4 * n * n,

@@ -1,0 +1,86 @@
+"""Host logic of the benchmark, on the CPU: the algorithmic byte counts the
+roofline is priced with, the selection of counter records, and the refusal
+of more than one GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from synth import workloads as W  # noqa: E402
+
+NAMES = ["c1", "c2", "c3", "c4", "c5"]
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_step_bytes_follow_the_per_element_terms(name):
+    """Per (element, worker): gradient, compensated momentum in and out, sign
+    word out and read back by the server (gb + 8.25); per element: momentum
+    words read by each worker-pass launch, server u in and out and its words
+    out, update words, x in and out and v in (20.375 with one launch).  The
+    step must equal d*[n*(gb + 8.25) + 20.375] + (launches - 1)*d/8 plus the
+    segment partials and scales (momentum held as server sign words); the
+    fp32-momentum count is d*[n*(gb + 8.25) + 28.125]."""
+    w = W.make(name)
+    d, n = w.d, w.n
+    gb = 2 if w.bf16 else 4
+    nseg = -(-w.L // 1024)
+    ab = bench.alg_bytes(w)
+    assert set(ab) == {"worker", "worker_scale", "server", "server_scale", "update"}
+    partials = 2 * 8 * n * n * nseg + 2 * 8 * n * nseg  # written once, read once
+    small = 4 * n * n + 4 * n + 4 * n * n + 4 * n       # scales
+    launches = n if w.staged else 1
+    # exact in eighths: scale everything by 8
+    want8 = d * (n * (8 * gb + 66) + 163) + (launches - 1) * d + 8 * (partials + small)
+    assert 8 * sum(ab.values()) == want8
+    assert bench.fp32_momentum_step_bytes(w) == d * (n * (gb + 8.25) + 28.125)
+    # with one worker-pass launch, the compact layout moves fewer bytes than
+    # the fp32-momentum count (per-worker launches re-read the momentum words)
+    if not w.staged:
+        assert sum(ab.values()) < bench.fp32_momentum_step_bytes(w)
+
+
+def test_bytes_match_the_stated_c2_figures():
+    ab = bench.alg_bytes(W.make("c2"))
+    assert ab["worker"] == 8930635520
+    assert sum(ab.values()) == 11276732736
+
+
+def test_traffic_records_are_per_workload_and_kernel_code(tmp_path, monkeypatch):
+    sha = bench.kernel_sha()
+    rec = {"workload": "c3", "kernel_source_sha": sha, "kernel": "worker pass",
+           "bytes_per_launch": 123, "step_bytes": 456}
+    (tmp_path / "worker_pass_c3_counters.txt").write_text(
+        "summary\ntraffic_record: " + json.dumps(rec) + "\n")
+    stale = dict(rec, workload="c4", kernel_source_sha="0" * 16)
+    (tmp_path / "worker_pass_c4_counters.txt").write_text(
+        "traffic_record: " + json.dumps(stale) + "\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "worker_pass_%s_counters.txt"))
+    assert bench.load_traffic("c3")["bytes_per_launch"] == 123
+    assert bench.load_traffic("c4") is None   # taken on other kernel code
+    assert bench.load_traffic("c2") is None   # no record
+
+
+def test_committed_records_name_their_workload():
+    for name in NAMES:
+        path = bench.TRAFFIC_FILE % name
+        if not os.path.exists(path):
+            continue
+        lines = [ln for ln in open(path) if ln.startswith("traffic_record: ")]
+        assert len(lines) == 1
+        rec = json.loads(lines[0][len("traffic_record: "):])
+        assert rec["workload"] == name
+        assert rec["bytes_per_launch"] > 0 and rec["step_bytes"] >= rec["bytes_per_launch"]
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
