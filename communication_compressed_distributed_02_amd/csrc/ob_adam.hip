@@ -8,6 +8,7 @@
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <new>
 #include <vector>
@@ -559,7 +560,12 @@ ob_status ob_adam_destroy(ob_adam_t h) {
 }
 
 const char* ob_status_str(ob_status s) {
-  switch (s) {
+  // A C caller may pass any int: read the argument's bits as an int, since
+  // loading an out-of-range value through the enum type is undefined in C++.
+  static_assert(sizeof(ob_status) == sizeof(int), "ob_status is an int-sized enum");
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case OB_OK: return "ok";
     case OB_ERR_ARG: return "invalid argument";
     case OB_ERR_SHAPE:

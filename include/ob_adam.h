@@ -256,7 +256,7 @@ ob_status ob_adam_kernel_times(ob_adam_t h, double* ms /* [OB_NUM_KERNELS] */,
 /* Release the host handle (the caller frees the workspace afterwards). */
 ob_status ob_adam_destroy(ob_adam_t h);
 
-/* Static description of a status code. */
+/* Static description of a status code ("unknown status" for any other value). */
 const char* ob_status_str(ob_status s);
 
 #ifdef __cplusplus
