@@ -34,9 +34,13 @@
 //    of vector-loaded sign words puts in each lane; for other worker counts
 //    it folds the workers' +-s in worker order into per-row stacks.  Both
 //    reproduce the pairwise-by-levels sum exactly.
+//  - The worker pass folds the partials of a block's 4 aligned segments in
+//    LDS (the first two levels of the pairwise tree over a chunk's segment
+//    partials), so it writes one partial per block; the server pass writes
+//    one per segment.
 //  - Per-chunk scales come from small kernels: one dispatch that folds a
-//    chunk's segment partials in registers and one block, or aligned groups
-//    of 512 partials folded in parallel and then one block per chunk.
+//    chunk's partials in registers and one block, or aligned groups of 512
+//    partials folded in parallel and then one block per chunk.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -50,6 +54,12 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / 64;
 constexpr int64_t kMaxBlocksPerRow = int64_t(1) << 20;
+static_assert(kWavesPerBlock == 4, "the worker pass folds 4 segment partials per block");
+
+// Blocks of 4 aligned segments in a chunk of nseg segments.
+__host__ __device__ constexpr int64_t quads(int64_t nseg) {
+  return (nseg + kWavesPerBlock - 1) / kWavesPerBlock;
+}
 
 // Streamed (read-once / write-once per step) accesses are non-temporal: the
 // step's working set is many times the caches, so nothing streamed is reused
@@ -293,6 +303,13 @@ __device__ __forceinline__ void worker_row(const GT* __restrict__ g, float* __re
   acc = add_square(acc, cv);
 }
 
+// The block's 4 waves own 4 consecutive segments, aligned at a multiple of 4;
+// their partials are folded in LDS as ((p0 + p1) + (p2 + p3)), the first two
+// levels of the pairwise sum over a chunk's segment partials (a segment past
+// the chunk's end counts as +0, as the zero padding does), so one fp64
+// partial per block reaches HBM and the finalize folds 4x fewer.  The loop
+// over blocks' quads is uniform across the block, so every wave reaches
+// both barriers.
 template <typename GT, bool MBITS>
 __global__ void __launch_bounds__(kBlock)
     worker_kernel(GradPtrs g, int w0, int64_t d, int64_t L, int n, int64_t nseg, int64_t words,
@@ -300,48 +317,55 @@ __global__ void __launch_bounds__(kBlock)
                   const float* __restrict__ sscale, float* __restrict__ cbuf,
                   const float* __restrict__ wscale, uint64_t* __restrict__ wbits,
                   double* __restrict__ wpart, float beta1, float ob1) {
+  __shared__ double quad_part[kWavesPerBlock];
   const int lane = threadIdx.x & 63;
+  const int wv = wave_in_block();
   const int wi = (int)blockIdx.y / n;  // worker within this launch
   const int j = (int)blockIdx.y - wi * n;
   const int w = w0 + wi;
   const GT* __restrict__ gp = (const GT*)g.p[wi];
   float* __restrict__ c = cbuf + (int64_t)w * d;
   uint64_t* __restrict__ bits = wbits + (int64_t)w * words;
-  double* __restrict__ part = wpart + ((int64_t)w * n + j) * nseg;
+  const int64_t nquad = quads(nseg);
+  double* __restrict__ part = wpart + ((int64_t)w * n + j) * nquad;
   const float sp = wscale[w * n + j];  // this worker's scale of chunk j, previous step
   const float ms = MBITS ? sscale[j] : 0.0f;
-  const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); s < nseg;
-       s += nwave) {
-    const int64_t q0 = s * kSegElems;
-    const int64_t left = (L - q0) >> 6;
-    const int rows = left < kSegRows ? (int)left : kSegRows;
-    const int64_t base = (int64_t)j * L + q0;  // global index of the segment's first element
-    const int64_t wbase = base >> 6;
+  for (int64_t qd = blockIdx.x; qd < nquad; qd += gridDim.x) {
+    const int64_t s = qd * kWavesPerBlock + wv;
     double acc = 0.0;
-    uint64_t mine = 0;
-    if (rows == kSegRows) {
-      // fully unrolled: the compiler issues all 32 loads of the segment first
+    if (s < nseg) {
+      const int64_t q0 = s * kSegElems;
+      const int64_t left = (L - q0) >> 6;
+      const int rows = left < kSegRows ? (int)left : kSegRows;
+      const int64_t base = (int64_t)j * L + q0;  // global index of the segment's first element
+      const int64_t wbase = base >> 6;
+      uint64_t mine = 0;
+      if (rows == kSegRows) {
+        // fully unrolled: the compiler issues all 32 loads of the segment first
 #pragma unroll
-      for (int r = 0; r < kSegRows; ++r) {
-        uint64_t word;
-        const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
-        worker_row<GT, MBITS>(gp, c, m, mword, ms, base + 64 * r + lane, sp, beta1, ob1, acc,
-                              word);
-        mine = lane == r ? word : mine;
+        for (int r = 0; r < kSegRows; ++r) {
+          uint64_t word;
+          const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
+          worker_row<GT, MBITS>(gp, c, m, mword, ms, base + 64 * r + lane, sp, beta1, ob1, acc,
+                                word);
+          mine = lane == r ? word : mine;
+        }
+      } else {
+        for (int r = 0; r < rows; ++r) {
+          uint64_t word;
+          const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
+          worker_row<GT, MBITS>(gp, c, m, mword, ms, base + 64 * r + lane, sp, beta1, ob1, acc,
+                                word);
+          mine = lane == r ? word : mine;
+        }
       }
-    } else {
-      for (int r = 0; r < rows; ++r) {
-        uint64_t word;
-        const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
-        worker_row<GT, MBITS>(gp, c, m, mword, ms, base + 64 * r + lane, sp, beta1, ob1, acc,
-                              word);
-        mine = lane == r ? word : mine;
-      }
+      acc = butterfly(acc);
+      if (lane < rows) bits[wbase + lane] = mine;
     }
-    acc = butterfly(acc);
-    if (lane < rows) bits[wbase + lane] = mine;
-    if (lane == 0) part[s] = acc;
+    if (lane == 0) quad_part[wv] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) part[qd] = (quad_part[0] + quad_part[1]) + (quad_part[2] + quad_part[3]);
+    __syncthreads();
   }
 }
 
@@ -989,7 +1013,8 @@ static hipError_t launch_scales(const double* part, int64_t nseg, int64_t L, int
 }
 
 hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  return launch_scales(s.wpart, s.nseg, s.L, s.n * s.n, s.fold, s.wscale, stream, t0, t1);
+  // the worker pass leaves one partial per block of 4 segments
+  return launch_scales(s.wpart, quads(s.nseg), s.L, s.n * s.n, s.fold, s.wscale, stream, t0, t1);
 }
 
 hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
