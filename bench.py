@@ -45,8 +45,9 @@ def alg_bytes(w):
     d, n = w.d, w.n
     gb = 2 if w.bf16 else 4
     nseg = -(-w.L // 1024)
-    part_w = 8 * n * n * (-(-nseg // 4))  # one fp64 partial per block of 4 segments
-    part_s = 8 * n * nseg
+    nquad = -(-nseg // 4)  # one fp64 partial per block of 4 segments
+    part_w = 8 * n * n * nquad
+    part_s = 8 * n * nquad
     # worker-pass launches per step: one for all workers, or one per worker
     # when the gradients come one worker at a time (each launch reads the
     # momentum's sign words)

@@ -34,10 +34,9 @@
 //    of vector-loaded sign words puts in each lane; for other worker counts
 //    it folds the workers' +-s in worker order into per-row stacks.  Both
 //    reproduce the pairwise-by-levels sum exactly.
-//  - The worker pass folds the partials of a block's 4 aligned segments in
-//    LDS (the first two levels of the pairwise tree over a chunk's segment
-//    partials), so it writes one partial per block; the server pass writes
-//    one per segment.
+//  - The worker and server passes fold the partials of a block's 4 aligned
+//    segments in LDS (the first two levels of the pairwise tree over a
+//    chunk's segment partials), so they write one partial per block.
 //  - Per-chunk scales come from small kernels: one dispatch that folds a
 //    chunk's partials in registers and one block, or aligned groups of 512
 //    partials folded in parallel and then one block per chunk.
@@ -96,6 +95,18 @@ __device__ __forceinline__ double butterfly(double acc) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, 64);
   return acc;
+}
+
+// The partials of a block's 4 aligned segments (wave w's `acc`; 0 for a
+// segment past the chunk's end, like the zero padding) folded as
+// ((p0 + p1) + (p2 + p3)) -- the first two levels of the pairwise sum over
+// a chunk's segment partials -- and stored at *dst.  Every thread of the
+// block must reach it (it holds two barriers).
+__device__ __forceinline__ void store_quad_partial(double acc, double* quad_part, double* dst) {
+  if ((threadIdx.x & 63) == 0) quad_part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) *dst = (quad_part[0] + quad_part[1]) + (quad_part[2] + quad_part[3]);
+  __syncthreads();
 }
 
 // Pairwise sum by levels of N values (N a power of two), in place.
@@ -303,13 +314,11 @@ __device__ __forceinline__ void worker_row(const GT* __restrict__ g, float* __re
   acc = add_square(acc, cv);
 }
 
-// The block's 4 waves own 4 consecutive segments, aligned at a multiple of 4;
-// their partials are folded in LDS as ((p0 + p1) + (p2 + p3)), the first two
-// levels of the pairwise sum over a chunk's segment partials (a segment past
-// the chunk's end counts as +0, as the zero padding does), so one fp64
+// The block's 4 waves own 4 consecutive segments, aligned at a multiple of 4,
+// and their partials are folded in LDS (store_quad_partial), so one fp64
 // partial per block reaches HBM and the finalize folds 4x fewer.  The loop
-// over blocks' quads is uniform across the block, so every wave reaches
-// both barriers.
+// over the quads is uniform across the block, so every wave reaches the
+// barriers.
 template <typename GT, bool MBITS>
 __global__ void __launch_bounds__(kBlock)
     worker_kernel(GradPtrs g, int w0, int64_t d, int64_t L, int n, int64_t nseg, int64_t words,
@@ -362,10 +371,7 @@ __global__ void __launch_bounds__(kBlock)
       acc = butterfly(acc);
       if (lane < rows) bits[wbase + lane] = mine;
     }
-    if (lane == 0) quad_part[wv] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) part[qd] = (quad_part[0] + quad_part[1]) + (quad_part[2] + quad_part[3]);
-    __syncthreads();
+    store_quad_partial(acc, quad_part, part + qd);
   }
 }
 
@@ -552,52 +558,56 @@ __global__ void __launch_bounds__(kBlock)
     __syncthreads();
   }
   const float sp = sscale_prev[j];
-  const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); s < nseg;
-       s += nwave) {
-    const int64_t q0 = s * kSegElems;
-    const int64_t left = (L - q0) >> 6;
-    const int rows = left < kSegRows ? (int)left : kSegRows;
-    const int64_t base = (int64_t)j * L + q0;
-    const int64_t wbase = base >> 6;
-    double acc = 0.0;
-    uint64_t mine = 0;
-    if constexpr (NW > 0) {
-      if (rows == kSegRows) {
-        float up[kSegRows];
+  __shared__ double quad_part[kWavesPerBlock];
+  const int64_t nquad = quads(nseg);
+  for (int64_t qd = blockIdx.x; qd < nquad; qd += gridDim.x) {
+    const int64_t s = qd * kWavesPerBlock + wave_in_block();
+    // one segment: its sum of squares after the butterfly
+    auto segment = [&]() -> double {
+      double acc = 0.0;
+      const int64_t q0 = s * kSegElems;
+      const int64_t left = (L - q0) >> 6;
+      const int rows = left < kSegRows ? (int)left : kSegRows;
+      const int64_t base = (int64_t)j * L + q0;
+      const int64_t wbase = base >> 6;
+      uint64_t mine = 0;
+      if constexpr (NW > 0) {
+        if (rows == kSegRows) {
+          float up[kSegRows];
 #pragma unroll
-        for (int r = 0; r < kSegRows; ++r) up[r] = ld_stream(u + base + 64 * r + lane);
-        float avg[kSegRows];
-        server_average_segment<NW>(wbits, words, wbase, ws, avg);
+          for (int r = 0; r < kSegRows; ++r) up[r] = ld_stream(u + base + 64 * r + lane);
+          float avg[kSegRows];
+          server_average_segment<NW>(wbits, words, wbase, ws, avg);
 #pragma unroll
-        for (int r = 0; r < kSegRows; ++r) {
-          const float e = up[r] - (up[r] >= 0.0f ? sp : -sp);
-          const float uv = avg[r] + e;
-          st_stream(u + base + 64 * r + lane, uv);
-          const uint64_t word = __ballot(uv >= 0.0f);
-          mine = lane == r ? word : mine;
-          acc = add_square(acc, uv);
+          for (int r = 0; r < kSegRows; ++r) {
+            const float e = up[r] - (up[r] >= 0.0f ? sp : -sp);
+            const float uv = avg[r] + e;
+            st_stream(u + base + 64 * r + lane, uv);
+            const uint64_t word = __ballot(uv >= 0.0f);
+            mine = lane == r ? word : mine;
+            acc = add_square(acc, uv);
+          }
+          acc = butterfly(acc);
+          if (lane < kSegRows) sbits[wbase + lane] = mine;
+          return acc;
         }
-        acc = butterfly(acc);
-        if (lane < kSegRows) sbits[wbase + lane] = mine;
-        if (lane == 0) spart[(int64_t)j * nseg + s] = acc;
-        continue;
       }
-    }
-    for (int r = 0; r < rows; ++r) {
-      const int64_t k = base + 64 * r + lane;
-      const float up = u[k];
-      const float e = up - (up >= 0.0f ? sp : -sp);
-      const float a = worker_average<NW>(wbits, words, wbase + r, NW == 0 ? sws : ws, n);
-      const float uv = a + e;
-      u[k] = uv;
-      const uint64_t word = __ballot(uv >= 0.0f);
-      mine = lane == r ? word : mine;
-      acc = add_square(acc, uv);
-    }
-    acc = butterfly(acc);
-    if (lane < rows) sbits[wbase + lane] = mine;
-    if (lane == 0) spart[(int64_t)j * nseg + s] = acc;
+      for (int r = 0; r < rows; ++r) {
+        const int64_t k = base + 64 * r + lane;
+        const float up = u[k];
+        const float e = up - (up >= 0.0f ? sp : -sp);
+        const float a = worker_average<NW>(wbits, words, wbase + r, NW == 0 ? sws : ws, n);
+        const float uv = a + e;
+        u[k] = uv;
+        const uint64_t word = __ballot(uv >= 0.0f);
+        mine = lane == r ? word : mine;
+        acc = add_square(acc, uv);
+      }
+      acc = butterfly(acc);
+      if (lane < rows) sbits[wbase + lane] = mine;
+      return acc;
+    };
+    store_quad_partial(s < nseg ? segment() : 0.0, quad_part, spart + (int64_t)j * nquad + qd);
   }
 }
 
@@ -719,54 +729,59 @@ __global__ void __launch_bounds__(kBlock)
   }
   __syncthreads();
   const float sp = sscale_prev[j];
-  const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); s < nseg;
-       s += nwave) {
-    const int64_t q0 = s * kSegElems;
-    const int64_t left = (L - q0) >> 6;
-    const int rows = left < kSegRows ? (int)left : kSegRows;
-    const int64_t base = (int64_t)j * L + q0;
-    const int64_t wbase = base >> 6;
-    double acc = 0.0;
-    uint64_t mine = 0;
+  __shared__ double quad_part[kWavesPerBlock];
+  const int64_t nquad = quads(nseg);
+  for (int64_t qd = blockIdx.x; qd < nquad; qd += gridDim.x) {
+    const int64_t s = qd * kWavesPerBlock + wave_in_block();
+    // one segment: its sum of squares after the butterfly
+    auto segment = [&]() -> double {
+      const int64_t q0 = s * kSegElems;
+      const int64_t left = (L - q0) >> 6;
+      const int rows = left < kSegRows ? (int)left : kSegRows;
+      const int64_t base = (int64_t)j * L + q0;
+      const int64_t wbase = base >> 6;
+      double acc = 0.0;
+      uint64_t mine = 0;
 #pragma unroll
-    for (int h = 0; h < kSegRows / 8; ++h) {
-      const int nrows = rows - 8 * h;  // rows of this half (<= 0 past a chunk's end)
-      if (nrows <= 0) break;
-      float avg[8];
-      server_average_groups<NG>(wbits, words, wbase + 8 * h, nrows, tab, lane, avg);
-      if (nrows >= 8) {
-        float up[8];
+      for (int h = 0; h < kSegRows / 8; ++h) {
+        const int nrows = rows - 8 * h;  // rows of this half (<= 0 past a chunk's end)
+        if (nrows <= 0) break;
+        float avg[8];
+        server_average_groups<NG>(wbits, words, wbase + 8 * h, nrows, tab, lane, avg);
+        if (nrows >= 8) {
+          float up[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) up[r] = ld_stream(u + base + 64 * (8 * h + r) + lane);
+          for (int r = 0; r < 8; ++r) up[r] = ld_stream(u + base + 64 * (8 * h + r) + lane);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float e = up[r] - (up[r] >= 0.0f ? sp : -sp);
-          const float uv = avg[r] + e;
-          st_stream(u + base + 64 * (8 * h + r) + lane, uv);
-          const uint64_t word = __ballot(uv >= 0.0f);
-          mine = lane == 8 * h + r ? word : mine;
-          acc = add_square(acc, uv);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          if (r < nrows) {
-            const int64_t k = base + 64 * (8 * h + r) + lane;
-            const float up = u[k];
-            const float e = up - (up >= 0.0f ? sp : -sp);
+          for (int r = 0; r < 8; ++r) {
+            const float e = up[r] - (up[r] >= 0.0f ? sp : -sp);
             const float uv = avg[r] + e;
-            u[k] = uv;
+            st_stream(u + base + 64 * (8 * h + r) + lane, uv);
             const uint64_t word = __ballot(uv >= 0.0f);
             mine = lane == 8 * h + r ? word : mine;
             acc = add_square(acc, uv);
           }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            if (r < nrows) {
+              const int64_t k = base + 64 * (8 * h + r) + lane;
+              const float up = u[k];
+              const float e = up - (up >= 0.0f ? sp : -sp);
+              const float uv = avg[r] + e;
+              u[k] = uv;
+              const uint64_t word = __ballot(uv >= 0.0f);
+              mine = lane == 8 * h + r ? word : mine;
+              acc = add_square(acc, uv);
+            }
+          }
         }
       }
-    }
-    acc = butterfly(acc);
-    if (lane < rows) sbits[wbase + lane] = mine;
-    if (lane == 0) spart[(int64_t)j * nseg + s] = acc;
+      acc = butterfly(acc);
+      if (lane < rows) sbits[wbase + lane] = mine;
+      return acc;
+    };
+    store_quad_partial(s < nseg ? segment() : 0.0, quad_part, spart + (int64_t)j * nquad + qd);
   }
 }
 
@@ -1050,7 +1065,8 @@ hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0,
 }
 
 hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  return launch_scales(s.spart, s.nseg, s.L, s.n, s.fold, s.sscale, stream, t0, t1);
+  // the server passes leave one partial per block of 4 segments
+  return launch_scales(s.spart, quads(s.nseg), s.L, s.n, s.fold, s.sscale, stream, t0, t1);
 }
 
 hipError_t launch_update(const State& s, float lr, hipStream_t stream, hipEvent_t t0,
