@@ -47,7 +47,7 @@ def alg_bytes(w):
     nseg = -(-w.L // 1024)
     nquad = -(-nseg // 4)  # one fp64 partial per block of 4 segments
     part_w = 8 * n * n * nquad
-    part_s = 8 * n * nquad
+    part_s = 8 * n * (nseg if n in (32, 64) else nquad)  # per segment at 32 and 64 workers
     # worker-pass launches per step: one for all workers, or one per worker
     # when the gradients come one worker at a time (each launch reads the
     # momentum's sign words)

@@ -36,7 +36,8 @@
 //    reproduce the pairwise-by-levels sum exactly.
 //  - The worker and server passes fold the partials of a block's 4 aligned
 //    segments in LDS (the first two levels of the pairwise tree over a
-//    chunk's segment partials), so they write one partial per block.
+//    chunk's segment partials), so they write one partial per block; the
+//    server pass for 32 and 64 workers writes one per segment.
 //  - Per-chunk scales come from small kernels: one dispatch that folds a
 //    chunk's partials in registers and one block, or aligned groups of 512
 //    partials folded in parallel and then one block per chunk.
@@ -59,6 +60,10 @@ static_assert(kWavesPerBlock == 4, "the worker pass folds 4 segment partials per
 __host__ __device__ constexpr int64_t quads(int64_t nseg) {
   return (nseg + kWavesPerBlock - 1) / kWavesPerBlock;
 }
+
+// The server pass for 32 and 64 workers leaves one partial per segment; every
+// other pass leaves one per block of 4 segments.
+constexpr bool server_segment_partials(int n) { return n == 32 || n == 64; }
 
 // Streamed (read-once / write-once per step) accesses are non-temporal: the
 // step's working set is many times the caches, so nothing streamed is reused
@@ -708,7 +713,13 @@ __device__ __forceinline__ void server_average_groups(const uint64_t* __restrict
   }
 }
 
-template <int NG>
+// SEG_PARTIALS (32 and 64 workers, 4 segments per wave): a wave takes
+// segments strided by the grid and stores one partial per segment.  Folding
+// a quad's partials per block there needs a barrier per quad (the n = 64 pass
+// went 6 % slower) or a wave-contiguous order (19 % more sign-word fetches).
+// Otherwise the block's 4 waves take one segment each of a quad and fold
+// their partials in LDS.
+template <int NG, bool SEG_PARTIALS>
 __global__ void __launch_bounds__(kBlock)
     server_groups_kernel(int64_t L, int n, int64_t nseg, int64_t words,
                          const uint64_t* __restrict__ wbits, const float* __restrict__ wscale,
@@ -729,59 +740,68 @@ __global__ void __launch_bounds__(kBlock)
   }
   __syncthreads();
   const float sp = sscale_prev[j];
-  __shared__ double quad_part[kWavesPerBlock];
-  const int64_t nquad = quads(nseg);
-  for (int64_t qd = blockIdx.x; qd < nquad; qd += gridDim.x) {
-    const int64_t s = qd * kWavesPerBlock + wave_in_block();
-    // one segment: its sum of squares after the butterfly
-    auto segment = [&]() -> double {
-      const int64_t q0 = s * kSegElems;
-      const int64_t left = (L - q0) >> 6;
-      const int rows = left < kSegRows ? (int)left : kSegRows;
-      const int64_t base = (int64_t)j * L + q0;
-      const int64_t wbase = base >> 6;
-      double acc = 0.0;
-      uint64_t mine = 0;
+  // one segment: its sum of squares after the butterfly
+  auto segment = [&](int64_t s) -> double {
+    const int64_t q0 = s * kSegElems;
+    const int64_t left = (L - q0) >> 6;
+    const int rows = left < kSegRows ? (int)left : kSegRows;
+    const int64_t base = (int64_t)j * L + q0;
+    const int64_t wbase = base >> 6;
+    double acc = 0.0;
+    uint64_t mine = 0;
 #pragma unroll
-      for (int h = 0; h < kSegRows / 8; ++h) {
-        const int nrows = rows - 8 * h;  // rows of this half (<= 0 past a chunk's end)
-        if (nrows <= 0) break;
-        float avg[8];
-        server_average_groups<NG>(wbits, words, wbase + 8 * h, nrows, tab, lane, avg);
-        if (nrows >= 8) {
-          float up[8];
+    for (int h = 0; h < kSegRows / 8; ++h) {
+      const int nrows = rows - 8 * h;  // rows of this half (<= 0 past a chunk's end)
+      if (nrows <= 0) break;
+      float avg[8];
+      server_average_groups<NG>(wbits, words, wbase + 8 * h, nrows, tab, lane, avg);
+      if (nrows >= 8) {
+        float up[8];
 #pragma unroll
-          for (int r = 0; r < 8; ++r) up[r] = ld_stream(u + base + 64 * (8 * h + r) + lane);
+        for (int r = 0; r < 8; ++r) up[r] = ld_stream(u + base + 64 * (8 * h + r) + lane);
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const float e = up[r] - (up[r] >= 0.0f ? sp : -sp);
+        for (int r = 0; r < 8; ++r) {
+          const float e = up[r] - (up[r] >= 0.0f ? sp : -sp);
+          const float uv = avg[r] + e;
+          st_stream(u + base + 64 * (8 * h + r) + lane, uv);
+          const uint64_t word = __ballot(uv >= 0.0f);
+          mine = lane == 8 * h + r ? word : mine;
+          acc = add_square(acc, uv);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          if (r < nrows) {
+            const int64_t k = base + 64 * (8 * h + r) + lane;
+            const float up = u[k];
+            const float e = up - (up >= 0.0f ? sp : -sp);
             const float uv = avg[r] + e;
-            st_stream(u + base + 64 * (8 * h + r) + lane, uv);
+            u[k] = uv;
             const uint64_t word = __ballot(uv >= 0.0f);
             mine = lane == 8 * h + r ? word : mine;
             acc = add_square(acc, uv);
           }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            if (r < nrows) {
-              const int64_t k = base + 64 * (8 * h + r) + lane;
-              const float up = u[k];
-              const float e = up - (up >= 0.0f ? sp : -sp);
-              const float uv = avg[r] + e;
-              u[k] = uv;
-              const uint64_t word = __ballot(uv >= 0.0f);
-              mine = lane == 8 * h + r ? word : mine;
-              acc = add_square(acc, uv);
-            }
-          }
         }
       }
-      acc = butterfly(acc);
-      if (lane < rows) sbits[wbase + lane] = mine;
-      return acc;
-    };
-    store_quad_partial(s < nseg ? segment() : 0.0, quad_part, spart + (int64_t)j * nquad + qd);
+    }
+    acc = butterfly(acc);
+    if (lane < rows) sbits[wbase + lane] = mine;
+    return acc;
+  };
+  if constexpr (SEG_PARTIALS) {
+    const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); s < nseg;
+         s += nwave) {
+      const double p = segment(s);
+      if (lane == 0) spart[(int64_t)j * nseg + s] = p;
+    }
+  } else {
+    __shared__ double quad_part[kWavesPerBlock];
+    const int64_t nquad = quads(nseg);
+    for (int64_t qd = blockIdx.x; qd < nquad; qd += gridDim.x) {
+      const int64_t s = qd * kWavesPerBlock + wave_in_block();
+      store_quad_partial(s < nseg ? segment(s) : 0.0, quad_part, spart + (int64_t)j * nquad + qd);
+    }
   }
 }
 
@@ -1038,15 +1058,15 @@ hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0,
     // are built once per block)
     const int per_wave = s.n <= 16 ? 1 : 4;
     const dim3 grid(grid_for(s.nseg, kWavesPerBlock * per_wave, kMaxBlocksPerRow), (unsigned)s.n);
-#define OB_SRVG(NG)                                                                            \
-  return launch(server_groups_kernel<NG>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n, s.nseg, \
-                s.words, (const uint64_t*)s.wbits, (const float*)s.wscale, s.u,                 \
+#define OB_SRVG(NG, WQ)                                                                        \
+  return launch(server_groups_kernel<NG, WQ>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n,     \
+                s.nseg, s.words, (const uint64_t*)s.wbits, (const float*)s.wscale, s.u,         \
                 (const float*)s.sscale, s.sbits, s.spart)
     switch (s.n) {
-      case 8: OB_SRVG(1);
-      case 16: OB_SRVG(2);
-      case 32: OB_SRVG(4);
-      default: OB_SRVG(8);
+      case 8: OB_SRVG(1, false);
+      case 16: OB_SRVG(2, false);
+      case 32: OB_SRVG(4, server_segment_partials(32));
+      default: OB_SRVG(8, server_segment_partials(64));
     }
 #undef OB_SRVG
   }
@@ -1065,8 +1085,10 @@ hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0,
 }
 
 hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  // the server passes leave one partial per block of 4 segments
-  return launch_scales(s.spart, quads(s.nseg), s.L, s.n, s.fold, s.sscale, stream, t0, t1);
+  // the server passes leave one partial per block of 4 segments, or per
+  // segment with 32 and 64 workers
+  const int64_t count = server_segment_partials(s.n) ? s.nseg : quads(s.nseg);
+  return launch_scales(s.spart, count, s.L, s.n, s.fold, s.sscale, stream, t0, t1);
 }
 
 hipError_t launch_update(const State& s, float lr, hipStream_t stream, hipEvent_t t0,

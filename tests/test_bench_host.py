@@ -32,8 +32,9 @@ def test_step_bytes_follow_the_per_element_terms(name):
     nseg = -(-w.L // 1024)
     ab = bench.alg_bytes(w)
     assert set(ab) == {"worker", "worker_scale", "server", "server_scale", "update"}
-    nquad = -(-nseg // 4)  # both passes fold 4 segment partials per block
-    partials = 2 * 8 * n * n * nquad + 2 * 8 * n * nquad  # written once, read once
+    nquad = -(-nseg // 4)  # partials per block of 4 segments...
+    sparts = nseg if n in (32, 64) else nquad  # ...but per segment in the 32/64-worker server
+    partials = 2 * 8 * n * n * nquad + 2 * 8 * n * sparts  # written once, read once
     small = 4 * n * n + 4 * n + 4 * n * n + 4 * n       # scales
     launches = n if w.staged else 1
     # exact in eighths: scale everything by 8
