@@ -1001,9 +1001,10 @@ hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw,
 #undef OB_WORK
 }
 
-// Scales of `rows` rows of segment partials (nseg per row) into scale_out:
-// fold aligned groups of kGroup until at most kGroup values remain per row,
-// then the last fold and the scale.  `fold` holds rows *
+// Scales of `rows` rows of partials (`nseg` per row: one per segment, or one
+// per block of 4 segments, whose pairwise sums continue the same tree) into
+// scale_out: fold aligned groups of kGroup until at most kGroup values remain
+// per row, then the last fold and the scale.  `fold` holds rows *
 // fold_doubles_per_row(nseg) doubles.  t0 is taken at the first launch, t1
 // at the last.
 static hipError_t launch_scales(const double* part, int64_t nseg, int64_t L, int rows,
