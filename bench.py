@@ -1,22 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the 1-bit Adam compression-phase step on one MI355X.
 
-A step is one ob_adam_compressed_step over one batch of n workers' synthetic
+A step is one compressed step over one batch of n workers' synthetic
 gradients (all of the compressed step: worker compress, worker scales,
 server average/re-compress, server scales, decompress + frozen-variance
-update).  Default workload: d = 110,000,128 fp32 parameters (a BERT-Base
-sized flat vector), n = 8 simulated workers, bf16 gradients N(0, 1e-3),
-2 full-precision warm-up steps before the compressed ones.  All gradient
-batches are generated on the GPU before the timed region.
+update).
+Default workload: c5, the BERT-Large run on 64 data-parallel workers --
+d = 340,000,768 fp32 parameters, n = 64 simulated workers, fp32 gradients
+N(0, 1e-3), supplied one worker at a time (the staged entry points), 30
+full-precision warm-up steps before the compressed ones.  All gradients are
+generated on the GPU before the timed region.
 
 Prints one JSON line with:
 - params*workers/s of the whole step;
 - the worker pass's roofline against MI355X's 8 TB/s HBM peak, timed live
-  with HIP events the library records on its stream, plus the profiler's
-  byte counters when they were taken on the current kernel code;
+  with HIP events the library records on its stream, next to the same
+  figure from the committed kernel-trace average, plus the profiler's byte
+  counters when they were taken on the current kernel code;
 - the step's other kernels and streaming probes of the same access mix;
-- the CPU oracle timed on a bounded sample (chunk 0), and the comparison of
-  its state with the GPU's after the same steps (parity).
+- the CPU oracle timed on a bounded sample (chunk 0), and, when the sample
+  runs the same steps as the GPU, the comparison of the two states (parity).
 """
 import argparse
 import hashlib
@@ -36,6 +39,11 @@ METRIC = "compressed-step params·workers/sec and achieved HBM GB/s (% of peak),
 KERNEL_SRC = os.path.join(ROOT, "communication_compressed_distributed_02_amd", "csrc",
                           "ob_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "worker_pass_%s_counters.txt")  # % workload
+TRACE_FILE = os.path.join(ROOT, "profiles", "compressed_step_%s_kernel_trace.txt")  # % workload
+DEFAULT_WORKLOAD = "c5"
+# CPU-baseline budget: (warm-up + timed) oracle steps x n x L element-workers
+# (about 1e8 per second on one core)
+CPU_BUDGET = 2.5e9
 
 
 def alg_bytes(w):
@@ -82,14 +90,14 @@ def kernel_sha():
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """Counter-measured HBM bytes per worker-pass launch, if they were taken
-    on the current kernel source (else None)."""
+def _load_record(path, key, workload):
+    """The `key: {json}` record of a profile summary, if it was taken on the
+    current kernel source for this workload (else None)."""
     t = None
     try:
-        for line in open(TRAFFIC_FILE % workload):
-            if line.startswith("traffic_record: "):
-                t = json.loads(line[len("traffic_record: "):])
+        for line in open(path % workload):
+            if line.startswith(key + ": "):
+                t = json.loads(line[len(key) + 2:])
     except (OSError, ValueError):
         return None
     if t is None:
@@ -97,6 +105,18 @@ def load_traffic(workload):
     if t.get("kernel_source_sha") != kernel_sha() or t.get("workload") != workload:
         return None
     return t
+
+
+def load_traffic(workload):
+    """Counter-measured HBM bytes per worker-pass launch, if they were taken
+    on the current kernel source (else None)."""
+    return _load_record(TRAFFIC_FILE, "traffic_record", workload)
+
+
+def load_trace(workload):
+    """rocprofv3's average duration of a steady-state worker-pass launch, if
+    the trace was taken on the current kernel source (else None)."""
+    return _load_record(TRACE_FILE, "trace_record", workload)
 
 
 def host_cpu():
@@ -112,30 +132,46 @@ def host_cpu():
     return model, len(os.sched_getaffinity(0))
 
 
+def cpu_plan(w, steps):
+    """(warm-up steps, compressed steps) of the CPU baseline on chunk 0.  The
+    workload's own warm-up and `steps` compressed steps when the sample fits
+    CPU_BUDGET (then its state can be compared with the GPU's); else one
+    warm-up step and as many compressed steps as fit, at least one.  The
+    oracle's time per compressed step does not depend on the state it starts
+    from, so the shortened sample still times the same work per step."""
+    unit = w.n * w.L
+    if (w.warmup + steps) * unit <= CPU_BUDGET:
+        return w.warmup, steps
+    return 1, max(1, min(steps, int(CPU_BUDGET // unit) - 1))
+
+
 def cpu_baseline(w, steps=1, snap=None):
     """The CPU oracle on chunk 0 (all n workers, 1/n of the step's work),
-    timed over `steps` compressed steps after the warm-up, scaled by n.  The
-    calling thread is pinned to one core while the oracle runs.  With `snap`
-    (the GPU's chunk-0 state after the same steps on the same gradients) the
-    two are compared: returns (baseline, parity)."""
+    timed over the compressed steps of cpu_plan(), scaled by n.  The calling thread is pinned to one core while the
+    oracle runs.  With `snap` (the GPU's chunk-0 state after the same steps on
+    the same gradients) the two are compared: returns (baseline, parity)."""
     import oracle
     from synth import workloads as W
     L = w.L
+    warm, steps = cpu_plan(w, steps)
     model, usable = host_cpu()
     allowed = os.sched_getaffinity(0)
     core = min(allowed)
     os.sched_setaffinity(0, {core})
     try:
-        per_step, o = _oracle_step_seconds(oracle, W, w, L, steps)
+        per_step, o = _oracle_step_seconds(oracle, W, w, L, warm, steps)
     finally:
         os.sched_setaffinity(0, allowed)
     parity = compare_chunk0(oracle, o, snap, w) if snap is not None else None
     o.close()
+    short = "" if warm == w.warmup else (
+        " (the workload has %d warm-up steps; the sample starts its compressed steps after %d "
+        "to bound its run)" % (w.warmup, warm))
     return {"value": w.n * w.d / per_step, "unit": "params*workers/s", "cores": 1,
             "kind": "oracle",
             "sample": "chunk 0 of %d (%d elements x %d workers), %d compressed step(s) after "
-                      "%d warm-up steps, single thread pinned to core %d, time x%d for the "
-                      "whole step" % (w.n, L, w.n, steps, w.warmup, core, w.n),
+                      "%d warm-up step(s)%s, single thread pinned to core %d, time x%d for the "
+                      "whole step" % (w.n, L, w.n, steps, warm, short, core, w.n),
             "host_cpu": model, "host_cores_usable": usable,
             "s_per_step_extrapolated": per_step}, parity
 
@@ -186,17 +222,18 @@ def compare_chunk0(oracle, o, snap, w):
             "pass": bool(bits and scales and snap["step"] == o.step and ratio <= 1.0)}
 
 
-def _oracle_step_seconds(oracle, W, w, L, steps):
+def _oracle_step_seconds(oracle, W, w, L, warm, steps):
     o = oracle.Oracle(w.d, w.n, w.beta1, w.beta2, w.eps, j0=0, j1=1, keep_debug=False)
     secs = []
-    for t in range(w.warmup + steps):
+    for t in range(warm + steps):
         g = [W.cpu_grad(w, i, t, 0, L) for i in range(w.n)]
-        if t < w.warmup:
+        if t < warm:
             o.warmup_step(g, w.lr_at(t))
             continue
         t0 = time.perf_counter()
         o.compressed_step(g, w.lr_at(t))
         secs.append(time.perf_counter() - t0)
+        del g
     return sum(secs) / len(secs) * w.n, o
 
 
@@ -295,7 +332,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3, help="untimed compressed steps")
-    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=None,
                     help="compressed steps of the CPU baseline (default: --warmup, so that "
@@ -361,7 +398,8 @@ def main():
     torch.cuda.synchronize()
     cpu_steps = a.warmup if a.cpu_steps is None else a.cpu_steps
     snap = None
-    if not a.no_cpu_baseline and cpu_steps == a.warmup and ring >= w.warmup + a.warmup:
+    if (not a.no_cpu_baseline and cpu_steps == a.warmup and ring >= w.warmup + a.warmup
+            and cpu_plan(w, cpu_steps) == (w.warmup, cpu_steps)):
         # the untimed steps ran on each step's own gradients: keep chunk 0's
         # state for the comparison with the oracle after the same steps
         snap = snapshot_chunk0(opt, w)
@@ -383,7 +421,7 @@ def main():
     # Region 2: the same K steps again (the next steps of the run) with the
     # library's per-kernel HIP events, taken from the dispatch packets on its
     # stream; they add ~1.5 % to a step, so they stay out of region 1.
-    ob.ob_adam_set_timing(opt.h, (w.n + 4) * a.steps + 8)
+    ob.ob_adam_set_timing(opt.h, (w.n + 4) * a.steps + 8)  # launches per step: n + 4 at most
     f0 = torch.cuda.Event(enable_timing=True)
     f1 = torch.cuda.Event(enable_timing=True)
     f0.record()
@@ -412,6 +450,11 @@ def main():
         k["note"] = "staged: %d launches (one per worker) per step, summed" % per
     wk = kernels["worker"]
     traffic = load_traffic(w.name)
+    trace = load_trace(w.name)
+    # the same roofline from rocprofv3's average launch duration in the
+    # committed trace of this kernel code (per launch: bytes of one launch)
+    per_launch = ab["worker"] // (w.n if w.staged else 1)
+    trace_gbs = per_launch / (trace["avg_ns"] * 1e-9) / 1e9 if trace else None
     step_bytes = sum(ab.values())
     result = {
         "metric": METRIC,
@@ -432,12 +475,20 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "worker pass",
                      "achieved": round(wk["GB_s"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(wk["GB_s"] / HBM_PEAK_GBS, 4),
+                     "frac_source": "HIP events around every worker-pass launch of timing "
+                                    "region 2 (live, this run)",
+                     "achieved_from_trace": round(trace_gbs, 1) if trace else None,
+                     "frac_from_trace": round(trace_gbs / HBM_PEAK_GBS, 4) if trace else None,
+                     "trace_avg_us_per_launch": round(trace["avg_ns"] / 1e3, 2) if trace else None,
+                     "trace_kernel": trace["kernel"] if trace else None,
+                     "trace_file": os.path.relpath(TRACE_FILE % w.name, ROOT) if trace else None,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "copy-calibrated)",
                      "traffic_fetch": traffic["fetch_bytes_per_launch"] if traffic else None,
                      "traffic_write": traffic["write_bytes_per_launch"] if traffic else None,
-                     "alg_bytes_per_launch": wk["alg_bytes"]},
+                     "alg_bytes_per_launch": per_launch,
+                     "launches_per_step": w.n if w.staged else 1},
         "step": {"alg_bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                  "frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "fp32_momentum_bytes": fp32_momentum_step_bytes(w),

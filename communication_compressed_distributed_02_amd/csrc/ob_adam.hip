@@ -61,7 +61,10 @@ ob_status check_config(const ob_adam_config* cfg) {
     return OB_ERR_SHAPE;
   if (cfg->d % (64 * (int64_t)cfg->n_workers) != 0) return OB_ERR_SHAPE;
   const int64_t L = cfg->d / cfg->n_workers;
-  if ((L + ob::kSegElems - 1) / ob::kSegElems > ob::kMaxSegsPerChunk) return OB_ERR_SHAPE;
+  const int64_t nseg = (L + ob::kSegElems - 1) / ob::kSegElems;
+  if (nseg > ob::kMaxSegsPerChunk) return OB_ERR_SHAPE;
+  if ((cfg->n_workers == 32 || cfg->n_workers == 64) && nseg > ob::kMaxSegsPerChunkSegPartials)
+    return OB_ERR_SHAPE;
   return OB_OK;
 }
 
@@ -569,7 +572,8 @@ const char* ob_status_str(ob_status s) {
     case OB_OK: return "ok";
     case OB_ERR_ARG: return "invalid argument";
     case OB_ERR_SHAPE:
-      return "unsupported shape (need 0 < d <= 2^40, 1 <= n <= 64, d % (64*n) == 0, d/n <= 2^31)";
+      return "unsupported shape (need 0 < d <= 2^40, 1 <= n <= 64, d % (64*n) == 0, d/n <= 2^30, "
+             "and d/n <= 2^28 for n = 32 or 64)";
     case OB_ERR_PHASE: return "call out of order for the current phase";
     case OB_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case OB_ERR_HIP: return "HIP runtime error (handle poisoned)";

@@ -11,7 +11,10 @@ namespace ob {
 constexpr int kMaxWorkersPerLaunch = 64;
 constexpr int kSegElems = 1024;   // elements of one fixed-order segment (one wavefront)
 constexpr int kSegRows = 16;      // rows of 64 elements per segment
-constexpr int64_t kMaxSegsPerChunk = int64_t(1) << 21;
+constexpr int64_t kMaxSegsPerChunk = int64_t(1) << 20;  // chunks of at most 2^30 elements
+// With 32 and 64 workers the server pass leaves one partial per segment, and
+// its finalize folds at most 2^18 of them: chunks of at most 2^28 elements.
+constexpr int64_t kMaxSegsPerChunkSegPartials = int64_t(1) << 18;
 
 struct GradPtrs {
   const void* p[kMaxWorkersPerLaunch];

@@ -321,9 +321,9 @@ __device__ __forceinline__ void worker_row(const GT* __restrict__ g, float* __re
 
 // The block's 4 waves own 4 consecutive segments, aligned at a multiple of 4,
 // and their partials are folded in LDS (store_quad_partial), so one fp64
-// partial per block reaches HBM and the finalize folds 4x fewer.  The loop
-// over the quads is uniform across the block, so every wave reaches the
-// barriers.
+// partial per block reaches HBM and the finalize folds 4x fewer.  One block
+// per quad (grid.x == quads(nseg)): a grid-stride loop here, never taken
+// twice, held 42-50 VGPRs against 32-37 without it.
 template <typename GT, bool MBITS>
 __global__ void __launch_bounds__(kBlock)
     worker_kernel(GradPtrs g, int w0, int64_t d, int64_t L, int n, int64_t nseg, int64_t words,
@@ -344,7 +344,8 @@ __global__ void __launch_bounds__(kBlock)
   double* __restrict__ part = wpart + ((int64_t)w * n + j) * nquad;
   const float sp = wscale[w * n + j];  // this worker's scale of chunk j, previous step
   const float ms = MBITS ? sscale[j] : 0.0f;
-  for (int64_t qd = blockIdx.x; qd < nquad; qd += gridDim.x) {
+  {
+    const int64_t qd = blockIdx.x;  // one quad per block (grid.x == nquad)
     const int64_t s = qd * kWavesPerBlock + wv;
     double acc = 0.0;
     if (s < nseg) {
@@ -390,17 +391,17 @@ __global__ void __launch_bounds__(kBlock)
 // the same value as its own power-of-two width.
 constexpr int kGroup = 2 * kBlock;
 
-// Group results per row over all fold levels of a row of nseg partials.
+// Group results per row of nseg partials (0 when one block folds the row).
 int64_t fold_doubles_per_row(int64_t nseg) {
-  int64_t total = 0;
-  for (int64_t cnt = nseg;;) {
-    int64_t width = 1;
-    while (width < cnt) width <<= 1;
-    if (width <= kGroup) return total;
-    cnt = width / kGroup;
-    total += cnt;
-  }
+  int64_t width = 1;
+  while (width < nseg) width <<= 1;
+  return width <= kGroup ? 0 : width / kGroup;
 }
+static_assert(quads(kMaxSegsPerChunk) <= (int64_t)kGroup * kGroup &&
+                  kMaxSegsPerChunkSegPartials <= (int64_t)kGroup * kGroup,
+              "one level of group folds leaves at most kGroup values per row");
+static_assert(quads(kMaxSegsPerChunk) <= kMaxBlocksPerRow,
+              "the worker and server passes launch one block per quad of a row");
 
 // Pairwise fold of the 2*kBlock values a[t], b[t] (t = thread) held as pairs
 // (a[t] = element 2t, b[t] = element 2t+1); returns the sum in thread 0.
@@ -565,7 +566,8 @@ __global__ void __launch_bounds__(kBlock)
   const float sp = sscale_prev[j];
   __shared__ double quad_part[kWavesPerBlock];
   const int64_t nquad = quads(nseg);
-  for (int64_t qd = blockIdx.x; qd < nquad; qd += gridDim.x) {
+  {
+    const int64_t qd = blockIdx.x;  // one quad per block (grid.x == nquad)
     const int64_t s = qd * kWavesPerBlock + wave_in_block();
     // one segment: its sum of squares after the butterfly
     auto segment = [&]() -> double {
@@ -798,10 +800,9 @@ __global__ void __launch_bounds__(kBlock)
   } else {
     __shared__ double quad_part[kWavesPerBlock];
     const int64_t nquad = quads(nseg);
-    for (int64_t qd = blockIdx.x; qd < nquad; qd += gridDim.x) {
-      const int64_t s = qd * kWavesPerBlock + wave_in_block();
-      store_quad_partial(s < nseg ? segment(s) : 0.0, quad_part, spart + (int64_t)j * nquad + qd);
-    }
+    const int64_t qd = blockIdx.x;  // one quad per block (grid.x == nquad)
+    const int64_t s = qd * kWavesPerBlock + wave_in_block();
+    store_quad_partial(s < nseg ? segment(s) : 0.0, quad_part, spart + (int64_t)j * nquad + qd);
   }
 }
 
@@ -1028,24 +1029,19 @@ static hipError_t launch_scales(const double* part, int64_t nseg, int64_t L, int
                     scale_out);
     return launch(scale_direct_kernel<64>, grid, block, stream, t0, t1, part, nseg, L, scale_out);
   }
-  const double* cur = part;
-  int64_t cnt = nseg;
-  double* out = fold;
-  for (;;) {
-    int64_t width = 1;
-    while (width < cnt) width <<= 1;
-    if (width <= kGroup) break;
-    const int64_t ngroups = width / kGroup;
-    hipError_t e = launch(fold_groups_kernel, dim3((unsigned)ngroups, (unsigned)rows),
-                          dim3(kBlock), stream, t0, nullptr, cur, cnt, ngroups, out);
-    if (e != hipSuccess) return e;
-    t0 = nullptr;
-    cur = out;
-    cnt = ngroups;
-    out += (int64_t)rows * ngroups;
-  }
-  return launch(scale_kernel, dim3((unsigned)rows), dim3(kBlock), stream, t0, t1, cur, cnt, L,
-                scale_out);
+  // a row of at most kGroup partials: one block per row
+  if (width <= kGroup)
+    return launch(scale_kernel, dim3((unsigned)rows), dim3(kBlock), stream, t0, t1, part, nseg, L,
+                  scale_out);
+  // longer rows: aligned groups of kGroup partials folded in parallel, then
+  // one block per row folds the group results (at most kGroup of them: a
+  // row holds at most kGroup^2 partials, by the shape rule)
+  const int64_t ngroups = width / kGroup;
+  hipError_t e = launch(fold_groups_kernel, dim3((unsigned)ngroups, (unsigned)rows), dim3(kBlock),
+                        stream, t0, nullptr, part, nseg, ngroups, fold);
+  if (e != hipSuccess) return e;
+  return launch(scale_kernel, dim3((unsigned)rows), dim3(kBlock), stream, nullptr, t1,
+                (const double*)fold, ngroups, L, scale_out);
 }
 
 hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {

@@ -85,7 +85,8 @@ enum { OB_GRAD_F32 = 0, OB_GRAD_BF16 = 1 };
 
 typedef struct {
   int64_t d;          /* parameters; 0 < d <= 2^40, d % (64*n_workers) == 0 and
-                         d / n_workers <= 2^31 (chunk length) */
+                         d / n_workers <= 2^30 (chunk length; <= 2^28 for 32
+                         and 64 workers) */
   int32_t n_workers;  /* simulated workers; 1 <= n_workers <= 64 */
   int32_t grad_dtype; /* OB_GRAD_F32 or OB_GRAD_BF16 (bf16 is widened exactly) */
   float beta1, beta2, eps;

@@ -48,10 +48,14 @@ def test_workspace_bytes_and_shape_rules(ob):
     b = ob.ob_adam_workspace_bytes(ob.make_config(1 << 20, 4))
     # x, m, v, u + 4 compensated slabs, dominant terms
     assert b >= 8 * 4 * (1 << 20)
-    # the largest shapes accepted: chunks of 2^31 elements (64 workers: d = 2^37)
-    assert ob.ob_adam_workspace_bytes(ob.make_config(1 << 37, 64)) > 64 * 4 * (1 << 37)
+    # the largest shapes accepted: chunks of 2^30 elements (16 workers: d =
+    # 2^34), of 2^28 with 32 or 64 workers (64 workers: d = 2^34)
+    assert ob.ob_adam_workspace_bytes(ob.make_config(1 << 34, 16)) > 16 * 4 * (1 << 34)
+    assert ob.ob_adam_workspace_bytes(ob.make_config(1 << 34, 64)) > 64 * 4 * (1 << 34)
+    assert ob.ob_adam_workspace_bytes(ob.make_config(1 << 30, 1)) > 4 * (1 << 30)
     for d, n in ((1000, 4), (64 * 4 + 64, 4), (0, 1), (64 * 65, 65), (64, 0), (-64, 1),
-                 ((1 << 31) + 64, 1), ((1 << 37) + 64 * 64, 64), ((1 << 40) + 64, 64)):
+                 ((1 << 30) + 64, 1), ((1 << 34) + 64 * 64, 64), ((1 << 33) + 64 * 32, 32),
+                 ((1 << 34) + 64 * 16, 16), ((1 << 40) + 64, 64)):
         with pytest.raises(ob.ObAdamError) as e:
             ob.ob_adam_workspace_bytes(ob.make_config(d, n))
         assert e.value.status == ob.OB_ERR_SHAPE

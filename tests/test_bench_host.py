@@ -53,6 +53,35 @@ def test_bytes_match_the_stated_c2_figures():
     assert sum(ab.values()) == 11265130944
 
 
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("steps", [1, 3, 5, 20])
+def test_cpu_baseline_sample_is_bounded(name, steps):
+    """The CPU leg's oracle work stays within its budget (or is the least
+    sample there is: one warm-up and one compressed step), and keeps the
+    workload's own warm-up and the requested steps (so that its state can be
+    compared with the GPU's) wherever they fit."""
+    w = W.make(name)
+    warm, k = bench.cpu_plan(w, steps)
+    unit = w.n * w.L
+    assert 1 <= k <= steps
+    assert (warm + k) * unit <= bench.CPU_BUDGET or (warm, k) == (1, 1)
+    if (w.warmup + steps) * unit <= bench.CPU_BUDGET:
+        assert (warm, k) == (w.warmup, steps)
+    else:
+        assert warm == 1
+
+
+def test_default_workload_is_the_largest_config():
+    """The headline runs the 64-worker BERT-Large workload: the most
+    params x workers and the most bytes per step of all workloads."""
+    def size(nm):
+        w = W.make(nm)
+        return w.n * w.d, sum(bench.alg_bytes(w).values())
+    assert bench.DEFAULT_WORKLOAD == "c5"
+    for nm in NAMES:
+        assert size(nm) <= size("c5")
+
+
 def test_traffic_records_are_per_workload_and_kernel_code(tmp_path, monkeypatch):
     sha = bench.kernel_sha()
     rec = {"workload": "c3", "kernel_source_sha": sha, "kernel": "worker pass",

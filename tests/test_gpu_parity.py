@@ -2,8 +2,8 @@
 
 Sizes are chosen so the oracle finishes in seconds while the kernels see
 several segments, a ragged last segment (chunk length not a multiple of
-1024), chunks shorter than one segment, more segment partials than one
-finalize pass folds, generic (non power of two) worker counts with 2 to 4
+1024), chunks shorter than one segment, rows of one to 65 groups of the
+in-pass scale finalize, generic (non power of two) worker counts with 2 to 4
 levels of partial sums left for the final fold, bf16
 gradients, the first compressed step (fp32 momentum) and later ones
 (momentum kept as server sign words)."""
@@ -46,8 +46,15 @@ CASES = [
     ("n11_generic", 11 * 1088, 11, False, 1e-2, 2, 3),
     ("n24_generic_bf16", 24 * 1152, 24, True, 1e-3, 2, 3),
     ("n48_generic", 48 * 1088, 48, False, 1e-3, 1, 3),
-    ("n2_two_fold_groups", 2 * 614976, 2, False, 1e-2, 1, 3),
-    ("n1_eight_fold_groups", 3072064, 1, True, 1e-3, 1, 2),
+    # rows of the in-pass scale finalize: one group of 256 partials, two
+    # (ragged), three, and 65 (the row fold then takes two chunks of 64
+    # group sums); server rows of one partial per segment in two groups
+    ("n1_256_partials_one_group", 1048576, 1, True, 1e-3, 1, 2),
+    ("n1_257_partials_two_groups", 1048640, 1, False, 1e-2, 1, 2),
+    ("n2_two_groups_ragged", 2 * 1230208, 2, False, 1e-2, 1, 3),
+    ("n1_three_groups", 3072064, 1, True, 1e-3, 1, 2),
+    ("n1_65_groups", 67114048, 1, False, 1e-3, 1, 2),
+    ("n32_segment_partials_two_groups", 32 * 263232, 32, True, 1e-3, 1, 2),
 ]
 
 
