@@ -10,10 +10,43 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "ob_kernels.h"
+
+namespace {
+
+// Scratch of ob_adam_compressed_step_static: the step's fixed-order partials
+// and finalize group results live here instead of in the caller's
+// workspace.  One copy per GPU, held until the process ends.  Host code
+// never passes `scratch` itself to a kernel (in host code the name stands
+// for a host-side shadow, not a device address): static_scratch() looks up
+// its device address once per device with hipGetSymbolAddress and keeps it.
+constexpr uint64_t kStaticScratchBytes = uint64_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on `device` (which must be current).
+hipError_t static_scratch(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
+}  // namespace
 
 struct ob_adam_handle {
   ob::State st{};
@@ -29,6 +62,7 @@ struct ob_adam_handle {
   int warm_next = 0;          // the next worker that step expects
   bool poisoned = false;
   int32_t debug = 0;          // OB_DEBUG_* flags
+  int device = -1;            // the workspace's device, once a static-scratch step asked
   // per-kernel timing (events recorded around each launch when enabled)
   std::vector<hipEvent_t> ev;          // 2 per timed launch
   std::vector<int> ev_kernel;          // kernel id of each timed launch
@@ -178,9 +212,9 @@ void bias_corrections(const ob::State& s, int64_t t, float* bc1, float* bc2) {
   *bc2 = (float)(1.0 - p2);
 }
 
-// Worker scales, server pass, server scales, update; then count the step.
-ob_status finish_step(ob_adam_t h, float lr) {
-  const ob::State& s = h->st;
+// Worker scales, server pass, server scales, update on state `s` (the
+// handle's, or the handle's with its scratch elsewhere); then count the step.
+ob_status finish_step(ob_adam_t h, const ob::State& s, float lr) {
   hipStream_t st = h->stream;
   hipError_t e = timed(h, OB_K_WORKER_SCALE, [&](hipEvent_t a, hipEvent_t b) {
     return ob::launch_worker_scales(s, st, a, b);
@@ -379,7 +413,38 @@ ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float l
               return ob::launch_worker_pass(h->st, g, 0, h->st.n, m_bits, h->stream, a, b);
             }));
   if (st != OB_OK) return st;
-  return finish_step(h, lr);
+  return finish_step(h, h->st, lr);
+}
+
+ob_status ob_adam_compressed_step_static(ob_adam_t h, const void* const* grads, float lr) {
+  ob_status st = usable(h);
+  if (st != OB_OK) return st;
+  const ob::ScratchLayout sl = ob::scratch_layout(h->st.nseg, h->st.n);
+  if (sl.total > kStaticScratchBytes) return OB_ERR_TOO_LARGE;
+  if (h->warm == 0 || any_open(h)) return OB_ERR_PHASE;
+  ob::GradPtrs g{};
+  st = gather_grads(h, grads, 0, h->st.n, &g);
+  if (st != OB_OK) return st;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(h, hipErrorNoDevice);
+  if (h->device < 0) {
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, h->base) != hipSuccess) return fail(h, hipErrorUnknown);
+    h->device = attr.device;
+  }
+  if (cur != h->device) return OB_ERR_ARG;  // the scratch must be the workspace's GPU's
+  void* base = nullptr;
+  if (static_scratch(cur, &base) != hipSuccess) return fail(h, hipErrorInvalidSymbol);
+  ob::State s = h->st;
+  s.wpart = (double*)((char*)base + sl.wpart);
+  s.spart = (double*)((char*)base + sl.spart);
+  s.fold = (double*)((char*)base + sl.fold);
+  const bool m_bits = h->compressed > 0;
+  st = fail(h, timed(h, OB_K_WORKER, [&](hipEvent_t a, hipEvent_t b) {
+              return ob::launch_worker_pass(s, g, 0, s.n, m_bits, h->stream, a, b);
+            }));
+  if (st != OB_OK) return st;
+  return finish_step(h, s, lr);
 }
 
 ob_status ob_adam_compress_worker(ob_adam_t h, int32_t worker, const void* grad) {
@@ -407,7 +472,7 @@ ob_status ob_adam_compressed_finish(ob_adam_t h, float lr) {
   if (st != OB_OK) return st;
   const uint64_t all = h->st.n == 64 ? ~(uint64_t)0 : (((uint64_t)1 << h->st.n) - 1);
   if (!h->staged_open || h->staged_mask != all) return OB_ERR_PHASE;
-  st = finish_step(h, lr);  // errors here leave the handle poisoned
+  st = finish_step(h, h->st, lr);  // errors here leave the handle poisoned
   h->staged_open = false;
   h->staged_mask = 0;
   return st;
@@ -577,6 +642,8 @@ const char* ob_status_str(ob_status s) {
     case OB_ERR_PHASE: return "call out of order for the current phase";
     case OB_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case OB_ERR_HIP: return "HIP runtime error (handle poisoned)";
+    case OB_ERR_TOO_LARGE:
+      return "the step's scratch exceeds the library's static scratch (32 MiB per GPU)";
   }
   return "unknown status";
 }

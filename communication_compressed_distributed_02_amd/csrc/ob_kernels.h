@@ -54,6 +54,15 @@ struct Layout {
 };
 Layout layout_for(int64_t d, int n);
 
+// The step's scratch (fixed-order partials of the workers and the server and
+// the finalize's group results) laid out in one region of its own: byte
+// offsets (256-byte aligned) and total.  layout_for reserves the same
+// buffers (at least as large) inside the workspace.
+struct ScratchLayout {
+  uint64_t wpart, spart, fold, total;
+};
+ScratchLayout scratch_layout(int64_t nseg, int n);
+
 // t0 / t1: optional timing events recorded at the start of the first and the
 // end of the last dispatch of the launcher (null = untimed).
 hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1, float bc2,

@@ -924,6 +924,20 @@ Layout layout_for(int64_t d, int n) {
   return l;
 }
 
+ScratchLayout scratch_layout(int64_t nseg, int n) {
+  const uint64_t un = (uint64_t)n;
+  const int64_t wrow = quads(nseg);  // worker rows: one partial per block of 4 segments
+  const int64_t srow = server_segment_partials(n) ? nseg : quads(nseg);
+  const uint64_t wfold = un * un * (uint64_t)fold_doubles_per_row(wrow);
+  const uint64_t sfold = un * (uint64_t)fold_doubles_per_row(srow);
+  ScratchLayout l{};
+  l.wpart = 0;
+  l.spart = align256(l.wpart + 8 * un * un * (uint64_t)wrow);
+  l.fold = align256(l.spart + 8 * un * (uint64_t)srow);
+  l.total = align256(l.fold + 8 * (wfold > sfold ? wfold : sfold));
+  return l;
+}
+
 hipError_t launch_warmup(const State& s, const GradPtrs& g, float lr, float bc1, float bc2,
                          hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const float ob1 = 1.0f - s.beta1, ob2 = 1.0f - s.beta2;

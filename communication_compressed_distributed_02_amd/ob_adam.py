@@ -14,14 +14,16 @@ import torch  # loads the HIP runtime the library binds to
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libob_adam.so")
 
-OB_OK, OB_ERR_ARG, OB_ERR_SHAPE, OB_ERR_PHASE, OB_ERR_WORKSPACE, OB_ERR_HIP = range(6)
+(OB_OK, OB_ERR_ARG, OB_ERR_SHAPE, OB_ERR_PHASE, OB_ERR_WORKSPACE, OB_ERR_HIP,
+ OB_ERR_TOO_LARGE) = range(7)
 OB_GRAD_F32, OB_GRAD_BF16 = 0, 1
 (OB_X, OB_M, OB_V, OB_E_WORKER, OB_E_SERVER, OB_BITS_WORKER, OB_BITS_SERVER, OB_SCALE_WORKER,
  OB_SCALE_SERVER) = range(9)
 
 EXPORTED = ("ob_adam_workspace_bytes", "ob_adam_init", "ob_adam_warmup_step",
             "ob_adam_warmup_worker", "ob_adam_warmup_finish",
-            "ob_adam_compressed_step", "ob_adam_compress_worker", "ob_adam_compressed_finish",
+            "ob_adam_compressed_step", "ob_adam_compressed_step_static",
+            "ob_adam_compress_worker", "ob_adam_compressed_finish",
             "ob_adam_get_state", "ob_adam_set_state", "ob_adam_params", "ob_adam_step_count",
             "ob_adam_get_counters", "ob_adam_attach", "ob_adam_check_guards", "ob_adam_set_debug",
             "ob_adam_set_timing",
@@ -57,6 +59,7 @@ def _load(path=LIB_PATH):
         "ob_adam_init": [cfgp, P, U64, P, P, ctypes.POINTER(P)],
         "ob_adam_warmup_step": [P, ctypes.POINTER(P), F],
         "ob_adam_compressed_step": [P, ctypes.POINTER(P), F],
+        "ob_adam_compressed_step_static": [P, ctypes.POINTER(P), F],
         "ob_adam_warmup_worker": [P, I32, P],
         "ob_adam_warmup_finish": [P, F],
         "ob_adam_compress_worker": [P, I32, P],
@@ -131,6 +134,11 @@ def ob_adam_warmup_finish(h, lr):
 
 def ob_adam_compressed_step(h, grad_ptrs, lr):
     _check(_lib.ob_adam_compressed_step(h, _ptr_array(grad_ptrs), lr), "ob_adam_compressed_step")
+
+
+def ob_adam_compressed_step_static(h, grad_ptrs, lr):
+    _check(_lib.ob_adam_compressed_step_static(h, _ptr_array(grad_ptrs), lr),
+           "ob_adam_compressed_step_static")
 
 
 def ob_adam_compress_worker(h, worker, grad_ptr):
@@ -293,6 +301,14 @@ class OneBitAdam:
         ptrs = self._grad_ptrs(grads)
         self._order_after_caller(*grads)
         ob_adam_compressed_step(self.h, ptrs, lr)
+        self._order_caller_after()
+
+    def compressed_step_static(self, grads, lr):
+        """compressed_step with the step's scratch in the library's static
+        array (allocates nothing)."""
+        ptrs = self._grad_ptrs(grads)
+        self._order_after_caller(*grads)
+        ob_adam_compressed_step_static(self.h, ptrs, lr)
         self._order_caller_after()
 
     def compress_worker(self, worker, grad):

@@ -77,7 +77,9 @@ typedef enum {
   OB_ERR_SHAPE = 2,     /* d, n do not satisfy the shape rule */
   OB_ERR_PHASE = 3,     /* call out of order (see each entry point) */
   OB_ERR_WORKSPACE = 4, /* workspace too small or misaligned */
-  OB_ERR_HIP = 5        /* HIP runtime error; the handle is poisoned */
+  OB_ERR_HIP = 5,       /* HIP runtime error; the handle is poisoned */
+  OB_ERR_TOO_LARGE = 6  /* the step's scratch exceeds the static scratch (see
+                           ob_adam_compressed_step_static) */
 } ob_status;
 
 /* Gradient element types. */
@@ -146,6 +148,32 @@ ob_status ob_adam_warmup_finish(ob_adam_t h, float lr);
  * captured gradients' addresses and lr.  The step counters count calls, so
  * replays are not counted. */
 ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float lr);
+
+/* The same step as ob_adam_compressed_step, for callers that cannot
+ * allocate device memory, or let anything allocate it, while they step (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): it allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine) and keeps the step's scratch -- the fixed-order partial
+ * sums of squares of the workers and of the server and the finalize's group
+ * results -- in a static array of the library's device code, 32 MiB per GPU,
+ * instead of in the workspace (whose own scratch region it leaves alone).
+ * The library's device code holds that array on every GPU it is loaded on
+ * until the process ends; its device address is looked up (once per GPU)
+ * on the first call on that GPU.  Results are identical to
+ * ob_adam_compressed_step (the same kernels).
+ *  - OB_ERR_TOO_LARGE, before anything is enqueued, when the configuration's
+ *    scratch exceeds 32 MiB (8 bytes per partial: n*n worker rows of
+ *    ceil(L/4096) partials, n server rows of ceil(L/4096) -- ceil(L/1024)
+ *    with 32 or 64 workers -- plus the group results of rows longer than
+ *    16384 partials; e.g. 1.56e9 params over 8 workers need 27 MiB);
+ *  - OB_ERR_ARG when the current device is not the workspace's;
+ *  - otherwise the errors and phase rules of ob_adam_compressed_step.
+ * Every call on one GPU shares that GPU's array, which keeps whatever the
+ * last call left there (nothing in it needs to start at zero: each step
+ * writes every partial before reading it).  Calls that overlap on one GPU
+ * -- two handles stepping on different streams at once -- race on the
+ * array: order them (one stream, or events). */
+ob_status ob_adam_compressed_step_static(ob_adam_t h, const void* const* grads, float lr);
 
 /* The same step with the gradients supplied one worker at a time, so that a
  * caller can regenerate each worker's gradient into one buffer (bounded

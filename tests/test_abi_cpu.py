@@ -79,7 +79,8 @@ def test_null_handle_is_an_argument_error(ob):
         ob.ob_adam_compressed_finish(None, 1e-3)
     assert e.value.status == ob.OB_ERR_ARG
     assert ob.ob_status_str(ob.OB_ERR_PHASE).startswith("call out of order")
-    for bad in (-1, 6, 99, 1 << 30):  # any int a C caller may pass
+    assert ob.ob_status_str(ob.OB_ERR_TOO_LARGE).startswith("the step's scratch exceeds")
+    for bad in (-1, 7, 99, 1 << 30):  # any int a C caller may pass
         assert ob.ob_status_str(bad) == "unknown status"
     with pytest.raises(ob.ObAdamError) as e:
         ob.ob_adam_set_debug(None, ob.OB_DEBUG_SYNC)
@@ -120,3 +121,57 @@ def test_header_compiles_as_c99():
             f.write(src)
         subprocess.check_call(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
                                "-fsyntax-only", "-I", os.path.join(ROOT, "include"), path])
+
+
+STATIC_SCRATCH = 32 << 20
+
+
+def static_scratch_bytes(d, n):
+    """The static-scratch step's scratch: worker partials (n*n rows of one
+    per 4 segments), server partials (n rows, one per segment with 32 or 64
+    workers), the larger of the two finalizes' group results; each buffer
+    256-byte aligned."""
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    def pow2(c):
+        w = 1
+        while w < c:
+            w *= 2
+        return w
+
+    def groups(c):
+        return 0 if pow2(c) <= 512 else pow2(c) // 512
+    nseg = -(-(d // n) // 1024)
+    wrow = -(-nseg // 4)
+    srow = nseg if n in (32, 64) else wrow
+    fold = max(n * n * groups(wrow), n * groups(srow))
+    return up(up(up(8 * n * n * wrow) + 8 * n * srow) + 8 * fold)
+
+
+@pytest.mark.parametrize("n,L", [(64, 4096 * 1024), (64, 4096 * 1025), (8, 194701440),
+                                 (16, 20882688), (1, 1 << 30), (32, 2 ** 21), (64, 5312512),
+                                 (16, 4096 * 8193), (16, 4096 * 8192)])
+def test_static_step_rejects_scratch_past_its_maximum_without_gpu(ob, n, L):
+    """ob_adam_compressed_step_static refuses a configuration whose scratch
+    exceeds the static 32 MiB before anything else (no GPU is touched: the
+    handle is attached to a workspace address that is never dereferenced);
+    one that fits reaches the phase rule (no warm-up step yet)."""
+    d = n * L
+    cfg = ob.make_config(d, n)
+    need = ob.ob_adam_workspace_bytes(cfg)
+    h = ob.ob_adam_attach(cfg, 256, need, (0, 0, 0), None)
+    try:
+        with pytest.raises(ob.ObAdamError) as e:
+            ob.ob_adam_compressed_step_static(h, [256] * n, 1e-3)
+        want = ob.OB_ERR_TOO_LARGE if static_scratch_bytes(d, n) > STATIC_SCRATCH else \
+            ob.OB_ERR_PHASE
+        assert e.value.status == want, (static_scratch_bytes(d, n), e.value.status)
+    finally:
+        ob.ob_adam_destroy(h)
+    # the benchmark workloads that take all gradients at once fit; the
+    # 64-worker one (gradients one worker at a time) does not
+    if (n, L) in ((8, 194701440), (16, 20882688)):
+        assert want == ob.OB_ERR_PHASE
+    if (n, L) == (64, 5312512):
+        assert want == ob.OB_ERR_TOO_LARGE
