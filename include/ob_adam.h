@@ -189,7 +189,15 @@ ob_status ob_adam_compressed_finish(ob_adam_t h, float lr);
  * OB_E_WORKER, OB_BITS_WORKER and OB_SCALE_WORKER of worker `worker`) into
  * device memory `dst_device`.  Derived fields (errors, decompressed momentum)
  * are materialized by a kernel.  Enqueued on the handle's stream; the range
- * must lie inside the field (OB_ERR_ARG otherwise).  OB_E_WORKER and
+ * must lie inside the field (OB_ERR_ARG otherwise).
+ * The destination is device memory and the call does not wait: a field of
+ * the large configurations is gigabytes, so the library neither stages it
+ * through host memory nor stalls the stream; a caller that wants it on the
+ * host copies the device buffer afterwards (the Python binding's get() returns
+ * a device tensor).  The step counter and the phase are not fields here:
+ * ob_adam_get_counters returns the steps taken, the compressed steps and the
+ * warm-up steps, and the phase follows from them (compression phase once a
+ * compressed step was taken).   OB_E_WORKER and
  * OB_BITS_WORKER are refused (OB_ERR_PHASE) while a worker-at-a-time
  * compressed step is open, as they would mix the old and the new step, and
  * OB_E_WORKER while a worker-at-a-time warm-up step is open. */
@@ -197,7 +205,14 @@ ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t 
                             int64_t count, void* dst_device);
 
 /* Overwrite `count` elements of OB_X (always) or OB_V (only before the first
- * compressed step) from device memory; OB_ERR_ARG for other fields. */
+ * compressed step) from device memory (enqueued, no wait); OB_ERR_ARG for
+ * other fields.  Only these two: every other field is either derived (the
+ * errors from the stored compensated values and scales, the momentum from
+ * the server's sign words and scales after the first compressed step) or
+ * must stay consistent with the sign words and scales the next step reads,
+ * and the frozen variance must not change once it preconditions compressed
+ * steps.  A whole state (all fields and the counters) is restored with
+ * ob_adam_attach from a copy of the workspace. */
 ob_status ob_adam_set_state(ob_adam_t h, int32_t field, int64_t offset, int64_t count,
                             const void* src_device);
 
