@@ -18,9 +18,10 @@ _LOAD_PATH = os.environ.get("OB_ORACLE_LIB", LIB_PATH)
 
 X, M, V, E_WORKER, E_SERVER, C_WORKER, U_SERVER, A_SERVER = range(8)
 BITS_WORKER, BITS_SERVER, SCALE_WORKER, SCALE_SERVER = 8, 9, 10, 11
+M_LOCAL, A_LOCAL, X_LOCAL = 12, 13, 14  # 0/1 Adam
 
 _FLOAT_FIELDS = {X, M, V, E_WORKER, E_SERVER, C_WORKER, U_SERVER, A_SERVER,
-                 SCALE_WORKER, SCALE_SERVER}
+                 SCALE_WORKER, SCALE_SERVER, M_LOCAL, A_LOCAL, X_LOCAL}
 
 
 def build(force=True):
@@ -52,6 +53,13 @@ def lib():
         for f in (L.ob_oracle_warmup_step, L.ob_oracle_compressed_step):
             f.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
                           ctypes.c_float]
+        L.ob_oracle_zo_step.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
+                                        ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                        ctypes.c_int32]
+        L.ob_oracle_zo_gamma.restype = ctypes.c_float
+        L.ob_oracle_zo_gamma.argtypes = [ctypes.c_void_p]
+        L.ob_oracle_zo_open.restype = ctypes.c_int32
+        L.ob_oracle_zo_open.argtypes = [ctypes.c_void_p]
         L.ob_oracle_field.restype = ctypes.c_void_p
         L.ob_oracle_field.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int64)]
@@ -137,6 +145,24 @@ class Oracle:
         keep, ptrs, dt = self._grad_ptrs(grads)
         lib().ob_oracle_compressed_step(self._h, ptrs, dt, lr)
         del keep
+
+    def zo_step(self, grads, lr, sync, refresh=False):
+        """One 0/1 Adam step (see ob_oracle_zo_step)."""
+        if refresh and not sync:
+            raise ValueError("the variance is refreshed only at a synchronizing step")
+        keep, ptrs, dt = self._grad_ptrs(grads)
+        lib().ob_oracle_zo_step(self._h, ptrs, dt, lr, 1 if sync else 0, 1 if refresh else 0)
+        del keep
+
+    @property
+    def zo_gamma(self):
+        """Sum of the step sizes of the open local period (fp32)."""
+        return np.float32(lib().ob_oracle_zo_gamma(self._h))
+
+    @property
+    def zo_open(self):
+        """Local steps taken in the open period (0 right after a synchronization)."""
+        return lib().ob_oracle_zo_open(self._h)
 
     def _view(self, field, worker=0):
         cnt = ctypes.c_int64(0)

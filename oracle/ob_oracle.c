@@ -33,6 +33,13 @@ struct ob_oracle {
   float *wscale;            /* [n][nch] */
   float *sscale;            /* [nch] */
   float *vals;              /* [n] scratch for the worker average */
+
+  /* 0/1 Adam (ob_oracle_zo_step), allocated on its first step */
+  float *mloc;              /* [n][cnt] each worker's local momentum */
+  float *aloc;              /* [n][cnt] each worker's step-weighted mean momentum */
+  float *xloc;              /* [cnt] scratch: one worker's local model */
+  float zgamma;             /* sum of the step sizes of the open local period */
+  int32_t zk;               /* local steps taken in the open period */
 };
 
 static float grad_at(const void* g, int32_t gdtype, int64_t k) {
@@ -182,6 +189,9 @@ void ob_oracle_destroy(ob_oracle* o) {
   free(o->wscale);
   free(o->sscale);
   free(o->vals);
+  free(o->mloc);
+  free(o->aloc);
+  free(o->xloc);
   free(o);
 }
 
@@ -211,42 +221,29 @@ void ob_oracle_warmup_step(ob_oracle* o, const void* const* grads, int32_t gdtyp
   }
 }
 
-/* Compression-phase step. */
-void ob_oracle_compressed_step(ob_oracle* o, const void* const* grads, int32_t gdtype, float lr) {
-  o->t += 1;
+/* Worker w, held chunk jj: compensated values c[0..L) (already formed) ->
+ * per-chunk scale, sign bits, new error e = c - (bit ? s : -s). */
+static void worker_compress_chunk(ob_oracle* o, int32_t w, int32_t jj, const float* c,
+                                  uint64_t* bits, float* e) {
+  const int64_t L = o->L;
+  const int64_t base = (int64_t)jj * L;
+  float s = ob_oracle_chunk_scale(ob_oracle_chunk_sumsq(c, L), L);
+  o->wscale[(size_t)w * (size_t)o->nch + jj] = s;
+  for (int64_t q = 0; q < L; ++q) {
+    int64_t k = base + q;
+    int bit = c[q] >= 0.0f;
+    set_bit(bits, k, bit);
+    e[k] = c[q] - (bit ? s : -s);
+  }
+}
+
+/* Server j (one per held chunk): average of the workers' decompressed
+ * chunks, plus its own error; scale, sign bits, new error.  Every worker
+ * then decompresses the server's chunk into m and updates x with the frozen
+ * v by `step` (the step's learning rate). */
+static void server_round(ob_oracle* o, float step) {
   const int32_t n = o->n;
   const int64_t L = o->L;
-  const int64_t cnt = o->cnt;
-  const float ob1 = 1.0f - o->beta1;
-
-  /* Worker i: momentum from the shared m and its own gradient, plus its error
-   * (error compensation); then per chunk: scale, sign bits, new error. */
-  memset(o->wbits, 0, sizeof(uint64_t) * (size_t)o->words * (size_t)n);
-  for (int32_t w = 0; w < n; ++w) {
-    float* e = o->e + (size_t)w * (size_t)cnt;
-    uint64_t* bits = o->wbits + (size_t)w * (size_t)o->words;
-    for (int32_t jj = 0; jj < o->nch; ++jj) {
-      int64_t base = (int64_t)jj * L;
-      float* c = o->keep_debug ? o->c + (size_t)w * (size_t)cnt + base : o->c;
-      for (int64_t q = 0; q < L; ++q) {
-        int64_t k = base + q;
-        float g = grad_at(grads[w], gdtype, k);
-        c[q] = ((o->beta1 * o->m[k]) + (ob1 * g)) + e[k];
-      }
-      float s = ob_oracle_chunk_scale(ob_oracle_chunk_sumsq(c, L), L);
-      o->wscale[(size_t)w * (size_t)o->nch + jj] = s;
-      for (int64_t q = 0; q < L; ++q) {
-        int64_t k = base + q;
-        int bit = c[q] >= 0.0f;
-        set_bit(bits, k, bit);
-        e[k] = c[q] - (bit ? s : -s);
-      }
-    }
-  }
-
-  /* Server j (one per chunk): average of the workers' decompressed chunks,
-   * plus its own error; scale, sign bits, new error.  Every worker then
-   * decompresses the server's chunk into m and updates x with the frozen v. */
   memset(o->sbits, 0, sizeof(uint64_t) * (size_t)o->words);
   for (int32_t jj = 0; jj < o->nch; ++jj) {
     int64_t base = (int64_t)jj * L;
@@ -270,9 +267,41 @@ void ob_oracle_compressed_step(ob_oracle* o, const void* const* grads, int32_t g
       float t = bit ? s : -s;
       o->e_srv[k] = u[q] - t;
       o->m[k] = t;
-      o->x[k] = o->x[k] - lr * (o->m[k] / (sqrtf(o->v[k]) + o->eps));
+      o->x[k] = o->x[k] - step * (o->m[k] / (sqrtf(o->v[k]) + o->eps));
     }
   }
+}
+
+/* Compression-phase step. */
+void ob_oracle_compressed_step(ob_oracle* o, const void* const* grads, int32_t gdtype, float lr) {
+  o->t += 1;
+  const int32_t n = o->n;
+  const int64_t L = o->L;
+  const int64_t cnt = o->cnt;
+  const float ob1 = 1.0f - o->beta1;
+
+  /* Worker i: momentum from the shared m and its own gradient, plus its error
+   * (error compensation); then per chunk: scale, sign bits, new error. */
+  memset(o->wbits, 0, sizeof(uint64_t) * (size_t)o->words * (size_t)n);
+  for (int32_t w = 0; w < n; ++w) {
+    float* e = o->e + (size_t)w * (size_t)cnt;
+    uint64_t* bits = o->wbits + (size_t)w * (size_t)o->words;
+    for (int32_t jj = 0; jj < o->nch; ++jj) {
+      int64_t base = (int64_t)jj * L;
+      float* c = o->keep_debug ? o->c + (size_t)w * (size_t)cnt + base : o->c;
+      for (int64_t q = 0; q < L; ++q) {
+        int64_t k = base + q;
+        float g = grad_at(grads[w], gdtype, k);
+        c[q] = ((o->beta1 * o->m[k]) + (ob1 * g)) + e[k];
+      }
+      worker_compress_chunk(o, w, jj, c, bits, e);
+    }
+  }
+
+  /* Server j (one per chunk): average of the workers' decompressed chunks,
+   * plus its own error; scale, sign bits, new error.  Every worker then
+   * decompresses the server's chunk into m and updates x with the frozen v. */
+  server_round(o, lr);
 }
 
 void* ob_oracle_field(ob_oracle* o, int32_t field, int32_t worker, int64_t* count) {
@@ -300,6 +329,19 @@ void* ob_oracle_field(ob_oracle* o, int32_t field, int32_t worker, int64_t* coun
     case OBO_BITS_SERVER: p = o->sbits; c = o->words; break;
     case OBO_SCALE_WORKER: p = o->wscale + w * (size_t)o->nch; c = o->nch; break;
     case OBO_SCALE_SERVER: p = o->sscale; c = o->nch; break;
+    case OBO_M_LOCAL:
+      if (o->mloc) { p = o->mloc + w * (size_t)cnt; c = cnt; }
+      break;
+    case OBO_A_LOCAL:
+      if (o->aloc) { p = o->aloc + w * (size_t)cnt; c = cnt; }
+      break;
+    case OBO_X_LOCAL:
+      if (o->xloc) {
+        ob_oracle_zo_local_model(o, (int32_t)w, o->xloc);
+        p = o->xloc;
+        c = cnt;
+      }
+      break;
     default: break;
   }
   if (count) *count = c;
@@ -308,3 +350,119 @@ void* ob_oracle_field(ob_oracle* o, int32_t field, int32_t worker, int64_t* coun
 
 int64_t ob_oracle_step(const ob_oracle* o) { return o->t; }
 int64_t ob_oracle_held(const ob_oracle* o) { return o->cnt; }
+
+
+/* ------------------------------------------------------------- 0/1 Adam --
+ * "Maximizing Communication Efficiency for Large-scale Training via 0/1
+ * Adam" (abstract): each Adam step is made linear by using stale estimates of
+ * the optimizer state and the linear correlation between the momentum and
+ * the model update; that linearity lets 1-bit compression and local steps
+ * (rounds without communication) be combined.  The abstract fixes no
+ * formula, so every step below is a reading (the design notes list them):
+ *  - stale state: the variance v is refreshed only at the steps the caller
+ *    flags, and only at a synchronizing step, by Adam's update on the
+ *    full-precision worker average of that step's gradients; between
+ *    refreshes it is frozen;
+ *  - local steps: between synchronizations every worker runs momentum steps
+ *    of its own, m_i = (b1*m_src) + ((1-b1)*g_i), with m_src the shared
+ *    momentum at the first step of a local period and m_i afterwards;
+ *  - linear correlation: with v frozen over the period, the worker's local
+ *    model is x_sync - G*(a_i/(sqrtf(v)+eps)), where G is the sum of the
+ *    period's step sizes and a_i the step-size-weighted mean of its momenta,
+ *    kept as a_1 = m_1, a_k = a_{k-1} + (w_k*(m_k - a_{k-1})), w_k = g_k/G_k;
+ *  - a synchronizing step sends a_i through the same 1-bit codec with error
+ *    feedback as the compressed step (c_i = a_i + e_i, per-chunk scales,
+ *    server average plus server error feedback); the decompressed server
+ *    output becomes the shared momentum, x_sync -= G*(m/(sqrtf(v)+eps)), and
+ *    the next step opens a new local period.
+ * With a synchronization at every step and no refresh, each step equals
+ * ob_oracle_compressed_step bit for bit (G = lr, a_i = m_i). */
+
+static int zo_ready(ob_oracle* o) {
+  if (o->mloc) return 1;
+  o->mloc = (float*)calloc((size_t)o->cnt * (size_t)o->n, sizeof(float));
+  o->aloc = (float*)calloc((size_t)o->cnt * (size_t)o->n, sizeof(float));
+  o->xloc = (float*)calloc((size_t)o->cnt, sizeof(float));
+  if (!o->mloc || !o->aloc || !o->xloc) abort();
+  o->zgamma = 0.0f;
+  o->zk = 0;
+  return 1;
+}
+
+void ob_oracle_zo_step(ob_oracle* o, const void* const* grads, int32_t gdtype, float lr,
+                       int32_t sync, int32_t refresh) {
+  zo_ready(o);
+  o->t += 1;
+  const int32_t n = o->n;
+  const int64_t L = o->L;
+  const int64_t cnt = o->cnt;
+  const float ob1 = 1.0f - o->beta1;
+  const int first = o->zk == 0;
+
+  /* the period's step sizes and this step's weight in the mean momentum */
+  o->zgamma = first ? lr : o->zgamma + lr;
+  const float wk = lr / o->zgamma;
+
+  /* local momentum step of every worker, and its step-weighted mean */
+  for (int32_t w = 0; w < n; ++w) {
+    float* ml = o->mloc + (size_t)w * (size_t)cnt;
+    float* al = o->aloc + (size_t)w * (size_t)cnt;
+    for (int64_t k = 0; k < cnt; ++k) {
+      float g = grad_at(grads[w], gdtype, k);
+      float msrc = first ? o->m[k] : ml[k];
+      float mi = (o->beta1 * msrc) + (ob1 * g);
+      ml[k] = mi;
+      al[k] = first ? mi : al[k] + (wk * (mi - al[k]));
+    }
+  }
+  o->zk += 1;
+  if (!sync) return;
+
+  /* Synchronization.  Workers: compensated mean momentum, then the
+   * compressed step's codec (per-chunk scale, sign bits, new error). */
+  memset(o->wbits, 0, sizeof(uint64_t) * (size_t)o->words * (size_t)n);
+  for (int32_t w = 0; w < n; ++w) {
+    float* e = o->e + (size_t)w * (size_t)cnt;
+    const float* al = o->aloc + (size_t)w * (size_t)cnt;
+    uint64_t* bits = o->wbits + (size_t)w * (size_t)o->words;
+    for (int32_t jj = 0; jj < o->nch; ++jj) {
+      int64_t base = (int64_t)jj * L;
+      float* c = o->keep_debug ? o->c + (size_t)w * (size_t)cnt + base : o->c;
+      for (int64_t q = 0; q < L; ++q) c[q] = al[base + q] + e[base + q];
+      worker_compress_chunk(o, w, jj, c, bits, e);
+    }
+  }
+
+  /* Server: average, server error, re-compression; the decompressed output
+   * is the shared momentum, and the shared model takes the period's summed
+   * step sizes with the stale variance. */
+  server_round(o, o->zgamma);
+
+  /* Variance refresh (after the update, which used the stale one):
+   * Adam's second-moment step on the full-precision average of this step's
+   * gradients. */
+  if (refresh) {
+    const float ob2 = 1.0f - o->beta2;
+    for (int64_t k = 0; k < cnt; ++k) {
+      for (int32_t w = 0; w < n; ++w) o->vals[w] = grad_at(grads[w], gdtype, k);
+      float gbar = ob_oracle_pairwise_mean(o->vals, n);
+      o->v[k] = (o->beta2 * o->v[k]) + (ob2 * (gbar * gbar));
+    }
+  }
+  o->zk = 0;
+}
+
+/* Worker w's local model: x_sync - G*(a_w/(sqrtf(v)+eps)) inside an open
+ * local period, x_sync right after a synchronization. */
+void ob_oracle_zo_local_model(ob_oracle* o, int32_t w, float* out) {
+  const float* al = o->aloc ? o->aloc + (size_t)w * (size_t)o->cnt : NULL;
+  for (int64_t k = 0; k < o->cnt; ++k) {
+    if (o->zk == 0 || !al)
+      out[k] = o->x[k];
+    else
+      out[k] = o->x[k] - o->zgamma * (al[k] / (sqrtf(o->v[k]) + o->eps));
+  }
+}
+
+float ob_oracle_zo_gamma(const ob_oracle* o) { return o->zgamma; }
+int32_t ob_oracle_zo_open(const ob_oracle* o) { return o->zk; }

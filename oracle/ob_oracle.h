@@ -19,6 +19,16 @@
  *    "What the evidence does not cover": the compressed allreduce.
  *  - "Adam: A Method for Stochastic Optimization" (listed under "Builds on"):
  *    the warm-up phase is that algorithm with bias correction.
+ *  - "Maximizing Communication Efficiency for Large-scale Training via 0/1
+ *    Adam" (abstract): the 0/1 Adam variant, ob_oracle_zo_step, built from the
+ *    same codec with local steps and a stale variance.  Its pins: with a
+ *    synchronization at every step and no refresh it equals the compressed
+ *    step bit for bit; local models equal a float64 re-derivation of the
+ *    sequential local steps; exact dyadic cases for the model averaging of a
+ *    synchronization and for the refresh.  Its readings (refresh schedule and
+ *    placement, the incremental step-weighted mean) are stated in
+ *    ob_oracle.c; beyond these pins the 0/1 trajectories are parity
+ *    unpinned.
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes of this repository):
@@ -61,7 +71,11 @@ enum {
   OBO_BITS_WORKER = 8, /* uint64[words] last sign words of worker w */
   OBO_BITS_SERVER = 9, /* uint64[words] last server sign words */
   OBO_SCALE_WORKER = 10, /* fp32[nch] last scales of worker w, one per held chunk */
-  OBO_SCALE_SERVER = 11  /* fp32[nch] last server scales */
+  OBO_SCALE_SERVER = 11, /* fp32[nch] last server scales */
+  /* 0/1 Adam (after its first ob_oracle_zo_step): */
+  OBO_M_LOCAL = 12,      /* fp32[cnt] local momentum of worker w */
+  OBO_A_LOCAL = 13,      /* fp32[cnt] step-weighted mean momentum of worker w */
+  OBO_X_LOCAL = 14       /* fp32[cnt] local model of worker w (computed on request) */
 };
 
 /* d % n must be 0; if the held range does not start at a multiple of 64 the
@@ -77,6 +91,23 @@ void ob_oracle_destroy(ob_oracle* o);
  * gdtype 0 = fp32, 1 = bf16 bit patterns (uint16). */
 void ob_oracle_warmup_step(ob_oracle* o, const void* const* grads, int32_t gdtype, float lr);
 void ob_oracle_compressed_step(ob_oracle* o, const void* const* grads, int32_t gdtype, float lr);
+
+/* One step of the 0/1 Adam variant ("Maximizing Communication Efficiency for
+ * Large-scale Training via 0/1 Adam", abstract), in the compression phase:
+ * every worker's local momentum step and step-weighted mean momentum; with
+ * `sync` the 1-bit compressed exchange of the mean momenta (error feedback on
+ * both sides, as in ob_oracle_compressed_step), the shared momentum and the
+ * shared model update by the local period's summed step sizes; with
+ * `refresh` (only together with sync) the variance's Adam update on the
+ * full-precision worker average of this step's gradients, after the model
+ * update.  The readings behind each part are stated in ob_oracle.c. */
+void ob_oracle_zo_step(ob_oracle* o, const void* const* grads, int32_t gdtype, float lr,
+                       int32_t sync, int32_t refresh);
+/* Worker w's local model into out[cnt]. */
+void ob_oracle_zo_local_model(ob_oracle* o, int32_t w, float* out);
+/* Sum of the step sizes of the open local period, and its steps so far. */
+float ob_oracle_zo_gamma(const ob_oracle* o);
+int32_t ob_oracle_zo_open(const ob_oracle* o);
 
 /* Pointer to a field (worker selects the slab for per-worker fields) and its
  * element count; the memory belongs to the oracle. */
