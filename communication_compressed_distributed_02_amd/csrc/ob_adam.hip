@@ -63,6 +63,12 @@ struct ob_adam_handle {
   bool poisoned = false;
   int32_t debug = 0;          // OB_DEBUG_* flags
   int device = -1;            // the workspace's device, once a static-scratch step asked
+  int32_t method = OB_METHOD_ONE_BIT;
+  // 0/1 Adam: the open local period (steps taken and their summed step sizes)
+  // and whether a synchronization has put the shared momentum into sign words
+  int32_t zk = 0;
+  float zgamma = 0.0f;
+  bool zsynced = false;
   // per-kernel timing (events recorded around each launch when enabled)
   std::vector<hipEvent_t> ev;          // 2 per timed launch
   std::vector<int> ev_kernel;          // kernel id of each timed launch
@@ -87,6 +93,7 @@ bool grad_aligned(const ob_adam_t h, const void* g) {
 ob_status check_config(const ob_adam_config* cfg) {
   if (cfg == nullptr) return OB_ERR_ARG;
   if (cfg->grad_dtype != OB_GRAD_F32 && cfg->grad_dtype != OB_GRAD_BF16) return OB_ERR_ARG;
+  if (cfg->method != OB_METHOD_ONE_BIT && cfg->method != OB_METHOD_ZERO_ONE) return OB_ERR_ARG;
   if (!valid_beta(cfg->beta1) || !valid_beta(cfg->beta2) || !isfinite(cfg->eps) ||
       cfg->eps < 0.0f)
     return OB_ERR_ARG;
@@ -242,7 +249,7 @@ ob_status ob_adam_workspace_bytes(const ob_adam_config* cfg, uint64_t* bytes) {
   ob_status st = check_config(cfg);
   if (st != OB_OK) return st;
   if (bytes == nullptr) return OB_ERR_ARG;
-  *bytes = ob::layout_for(cfg->d, cfg->n_workers).total;
+  *bytes = ob::layout_for(cfg->d, cfg->n_workers, cfg->method == OB_METHOD_ZERO_ONE).total;
   return OB_OK;
 }
 
@@ -250,7 +257,7 @@ namespace {
 
 // A handle over `workspace` (validated by the caller); nullptr if out of memory.
 ob_adam_handle* make_handle(const ob_adam_config* cfg, void* workspace, void* stream) {
-  const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers);
+  const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers, cfg->method == OB_METHOD_ZERO_ONE);
   ob_adam_handle* h = new (std::nothrow) ob_adam_handle();
   if (h == nullptr) return nullptr;
   char* base = (char*)workspace;
@@ -278,6 +285,11 @@ ob_adam_handle* make_handle(const ob_adam_config* cfg, void* workspace, void* st
   s.fold = (double*)(base + l.fold);
   s.wscale = (float*)(base + l.wscale);
   s.sscale = (float*)(base + l.sscale);
+  h->method = cfg->method;
+  if (cfg->method == OB_METHOD_ZERO_ONE) {
+    s.mloc = (float*)(base + l.mloc);
+    s.aloc = (float*)(base + l.aloc);
+  }
   h->stream = (hipStream_t)stream;
   const char* dbg = getenv("OB_DEBUG");
   if (dbg != nullptr) h->debug = atoi(dbg) & (OB_DEBUG_SYNC | OB_DEBUG_GUARDS);
@@ -285,7 +297,7 @@ ob_adam_handle* make_handle(const ob_adam_config* cfg, void* workspace, void* st
 }
 
 ob_status check_workspace(const ob_adam_config* cfg, void* workspace, uint64_t ws_bytes) {
-  const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers);
+  const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers, cfg->method == OB_METHOD_ZERO_ONE);
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0 || ws_bytes < l.total)
     return OB_ERR_WORKSPACE;
   return OB_OK;
@@ -302,7 +314,7 @@ ob_status ob_adam_init(const ob_adam_config* cfg, void* workspace, uint64_t ws_b
   if (st != OB_OK) return st;
   ob_adam_handle* h = make_handle(cfg, workspace, stream);
   if (h == nullptr) return OB_ERR_ARG;
-  const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers);
+  const ob::Layout l = ob::layout_for(cfg->d, cfg->n_workers, cfg->method == OB_METHOD_ZERO_ONE);
   const ob::State& s = h->st;
   hipError_t e = hipMemsetAsync(workspace, 0, l.total, h->stream);
   for (int i = 0; i < ob::kNumGuards && e == hipSuccess; ++i)
@@ -335,13 +347,16 @@ ob_status ob_adam_attach(const ob_adam_config* cfg, void* workspace, uint64_t ws
   h->steps = c.steps;
   h->compressed = c.compressed_steps;
   h->warm = c.warmup_steps;
+  // 0/1 Adam: counters are taken only between local periods, so every 0/1
+  // step before the checkpoint ended with (or was) a synchronization
+  h->zsynced = h->method == OB_METHOD_ZERO_ONE && c.compressed_steps > 0;
   *out = h;
   return OB_OK;
 }
 
 ob_status ob_adam_get_counters(ob_adam_t h, ob_adam_counters* out) {
   if (h == nullptr || out == nullptr) return OB_ERR_ARG;
-  if (any_open(h)) return OB_ERR_PHASE;
+  if (any_open(h) || h->zk > 0) return OB_ERR_PHASE;
   out->steps = h->steps;
   out->compressed_steps = h->compressed;
   out->warmup_steps = h->warm;
@@ -404,7 +419,7 @@ ob_status ob_adam_warmup_finish(ob_adam_t h, float lr) {
 ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float lr) {
   ob_status st = usable(h);
   if (st != OB_OK) return st;
-  if (h->warm == 0 || any_open(h)) return OB_ERR_PHASE;
+  if (h->warm == 0 || any_open(h) || h->method != OB_METHOD_ONE_BIT) return OB_ERR_PHASE;
   ob::GradPtrs g{};
   st = gather_grads(h, grads, 0, h->st.n, &g);
   if (st != OB_OK) return st;
@@ -421,7 +436,7 @@ ob_status ob_adam_compressed_step_static(ob_adam_t h, const void* const* grads, 
   if (st != OB_OK) return st;
   const ob::ScratchLayout sl = ob::scratch_layout(h->st.nseg, h->st.n);
   if (sl.total > kStaticScratchBytes) return OB_ERR_TOO_LARGE;
-  if (h->warm == 0 || any_open(h)) return OB_ERR_PHASE;
+  if (h->warm == 0 || any_open(h) || h->method != OB_METHOD_ONE_BIT) return OB_ERR_PHASE;
   ob::GradPtrs g{};
   st = gather_grads(h, grads, 0, h->st.n, &g);
   if (st != OB_OK) return st;
@@ -452,7 +467,7 @@ ob_status ob_adam_compress_worker(ob_adam_t h, int32_t worker, const void* grad)
   if (st != OB_OK) return st;
   if (worker < 0 || worker >= h->st.n || grad == nullptr || !grad_aligned(h, grad))
     return OB_ERR_ARG;
-  if (h->warm == 0 || h->warm_open) return OB_ERR_PHASE;
+  if (h->warm == 0 || h->warm_open || h->method != OB_METHOD_ONE_BIT) return OB_ERR_PHASE;
   const uint64_t bit = (uint64_t)1 << worker;
   if (h->staged_open && (h->staged_mask & bit)) return OB_ERR_PHASE;
   ob::GradPtrs g{};
@@ -478,13 +493,74 @@ ob_status ob_adam_compressed_finish(ob_adam_t h, float lr) {
   return st;
 }
 
+ob_status ob_adam_zero_one_step(ob_adam_t h, const void* const* grads, float lr,
+                                int32_t flags) {
+  ob_status st = usable(h);
+  if (st != OB_OK) return st;
+  if ((flags & ~(OB_ZO_SYNC | OB_ZO_REFRESH)) != 0) return OB_ERR_ARG;
+  const bool sync = (flags & OB_ZO_SYNC) != 0;
+  const bool refresh = (flags & OB_ZO_REFRESH) != 0;
+  if (refresh && !sync) return OB_ERR_ARG;
+  if (h->method != OB_METHOD_ZERO_ONE || h->warm == 0 || any_open(h)) return OB_ERR_PHASE;
+  ob::GradPtrs g{};
+  st = gather_grads(h, grads, 0, h->st.n, &g);
+  if (st != OB_OK) return st;
+  // the period's summed step sizes and this step's weight in the mean
+  // momentum, in fp32 as the method states them
+  const bool first = h->zk == 0;
+  const float gamma = first ? lr : h->zgamma + lr;
+  const float wk = lr / gamma;
+  const ob::State& s = h->st;
+  hipStream_t stm = h->stream;
+  if (!sync) {
+    st = fail(h, timed(h, OB_K_ZO_LOCAL, [&](hipEvent_t a, hipEvent_t b) {
+                return ob::launch_zo_local(s, g, first, h->zsynced, wk, stm, a, b);
+              }));
+    if (st != OB_OK) return st;
+    h->zk += 1;
+    h->zgamma = gamma;
+  } else {
+    hipError_t e = timed(h, OB_K_WORKER, [&](hipEvent_t a, hipEvent_t b) {
+      return ob::launch_zo_sync(s, g, first, h->zsynced, wk, stm, a, b);
+    });
+    if (e == hipSuccess)
+      e = timed(h, OB_K_WORKER_SCALE, [&](hipEvent_t a, hipEvent_t b) {
+        return ob::launch_worker_scales(s, stm, a, b);
+      });
+    if (e == hipSuccess)
+      e = timed(h, OB_K_SERVER,
+                [&](hipEvent_t a, hipEvent_t b) { return ob::launch_server_pass(s, stm, a, b); });
+    if (e == hipSuccess)
+      e = timed(h, OB_K_SERVER_SCALE, [&](hipEvent_t a, hipEvent_t b) {
+        return ob::launch_server_scales(s, stm, a, b);
+      });
+    if (e == hipSuccess)  // the shared model takes the whole period's steps
+      e = timed(h, OB_K_UPDATE,
+                [&](hipEvent_t a, hipEvent_t b) { return ob::launch_update(s, gamma, stm, a, b); });
+    if (e == hipSuccess && refresh)  // after the update, which used the stale variance
+      e = timed(h, OB_K_ZO_REFRESH,
+                [&](hipEvent_t a, hipEvent_t b) { return ob::launch_zo_refresh(s, g, stm, a, b); });
+    if (e != hipSuccess) return fail(h, e);
+    h->zk = 0;
+    h->zgamma = 0.0f;
+    h->zsynced = true;
+  }
+  h->steps += 1;
+  h->compressed += 1;
+  return after_step(h);
+}
+
 ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t offset,
                             int64_t count, void* dst_device) {
   ob_status st = usable(h);
   if (st != OB_OK) return st;
   const ob::State& s = h->st;
-  const bool per_worker =
-      field == OB_E_WORKER || field == OB_BITS_WORKER || field == OB_SCALE_WORKER;
+  const bool zo_field = field == OB_M_LOCAL || field == OB_A_LOCAL || field == OB_X_LOCAL;
+  if (zo_field && h->method != OB_METHOD_ZERO_ONE) return OB_ERR_ARG;
+  // the local momenta are the open local period's (none right after a sync)
+  if ((field == OB_M_LOCAL || field == OB_A_LOCAL) && h->zk == 0) return OB_ERR_PHASE;
+  const bool per_worker = field == OB_E_WORKER || field == OB_BITS_WORKER ||
+                          field == OB_SCALE_WORKER || zo_field;
   if (per_worker && (worker < 0 || worker >= s.n)) return OB_ERR_ARG;
   // mid-way through a worker-at-a-time step the compressed workers' slabs
   // already belong to the new step while the scales still belong to the old
@@ -494,7 +570,10 @@ ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t 
   if (h->warm_open && field == OB_E_WORKER) return OB_ERR_PHASE;
   int64_t size;
   switch (field) {
-    case OB_X: case OB_M: case OB_V: case OB_E_WORKER: case OB_E_SERVER: size = s.d; break;
+    case OB_X: case OB_M: case OB_V: case OB_E_WORKER: case OB_E_SERVER:
+    case OB_M_LOCAL: case OB_A_LOCAL: case OB_X_LOCAL:
+      size = s.d;
+      break;
     case OB_BITS_WORKER: case OB_BITS_SERVER: size = s.words; break;
     case OB_SCALE_WORKER: case OB_SCALE_SERVER: size = s.n; break;
     default: return OB_ERR_ARG;
@@ -514,7 +593,7 @@ ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t 
     case OB_X: e = copy(s.x, 4); break;
     case OB_V: e = copy(s.v, 4); break;
     case OB_M:
-      if (h->compressed > 0)
+      if (h->method == OB_METHOD_ZERO_ONE ? h->zsynced : h->compressed > 0)
         e = ob::launch_decompress_out(s.sbits, s.sscale, s.L, offset, count, (float*)dst_device,
                                       h->stream);
       else
@@ -531,6 +610,15 @@ ob_status ob_adam_get_state(ob_adam_t h, int32_t field, int32_t worker, int64_t 
     case OB_BITS_SERVER: e = copy(s.sbits, 8); break;
     case OB_SCALE_WORKER: e = copy(s.wscale + w * s.n, 4); break;
     case OB_SCALE_SERVER: e = copy(s.sscale, 4); break;
+    case OB_M_LOCAL: e = copy(s.mloc + w * s.d, 4); break;
+    case OB_A_LOCAL: e = copy(s.aloc + w * s.d, 4); break;
+    case OB_X_LOCAL:
+      if (h->zk == 0)
+        e = copy(s.x, 4);
+      else
+        e = ob::launch_zo_local_model(s.x, s.aloc + w * s.d, s.v, h->zgamma, s.eps, offset, count,
+                                      (float*)dst_device, h->stream);
+      break;
   }
   return fail(h, e);
 }

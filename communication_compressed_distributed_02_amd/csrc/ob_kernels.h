@@ -38,21 +38,25 @@ struct State {
   double* fold;       // [n][n][groups] group results of the scale finalize
   float* wscale;      // [n][n] row i = worker i, column j = chunk j
   float* sscale;      // [n]
+  float* mloc;        // [n][d]  0/1 Adam: each worker's local momentum (else null)
+  float* aloc;        // [n][d]  0/1 Adam: each worker's step-weighted mean momentum
 };
 
 // Workspace layout: byte offsets of each buffer (256-byte aligned) and total.
 // Every sub-buffer is followed directly by a guard region of kGuardBytes
 // holding a known pattern (guard i: 32-bit words guard_word(i)), so that a
 // write past a buffer's end can be detected from the host.
-constexpr int kNumGuards = 12;
+constexpr int kNumGuards = 14;
 constexpr uint64_t kGuardBytes = 256;
 constexpr uint32_t guard_word(int i) { return 0xA5C30000u + (uint32_t)i; }
 
 struct Layout {
-  uint64_t x, m, v, u, c, wbits, sbits, wpart, spart, fold, wscale, sscale, total;
+  uint64_t x, m, v, u, c, wbits, sbits, wpart, spart, fold, wscale, sscale, mloc, aloc, total;
   uint64_t guard[kNumGuards];  // offsets of the guards, in workspace order
 };
-Layout layout_for(int64_t d, int n);
+// zero_one: the 0/1 Adam variant's two per-worker slabs are reserved (else
+// they take no bytes; their guards are still there).
+Layout layout_for(int64_t d, int n, bool zero_one);
 
 // The step's scratch (fixed-order partials of the workers and the server and
 // the finalize's group results) laid out in one region of its own: byte
@@ -82,11 +86,25 @@ hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0,
 hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_update(const State& s, float lr, hipStream_t stream, hipEvent_t t0,
                          hipEvent_t t1);
+// 0/1 Adam: a local step of all workers (first: the first step of a local
+// period; m_bits: the shared momentum is held as server sign words), the
+// synchronizing step's worker pass (then worker scales, server pass, server
+// scales and launch_update with the period's summed step sizes), and the
+// variance refresh.  wk = lr / (the period's summed step sizes so far).
+hipError_t launch_zo_local(const State& s, const GradPtrs& g, bool first, bool m_bits, float wk,
+                           hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_zo_sync(const State& s, const GradPtrs& g, bool first, bool m_bits, float wk,
+                          hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_zo_refresh(const State& s, const GradPtrs& g, hipStream_t stream,
+                             hipEvent_t t0, hipEvent_t t1);
 
 // Materialize derived fields for readback.
 hipError_t launch_error_out(const float* comp, const float* scales, int64_t L, int64_t offset,
                             int64_t count, float* dst, hipStream_t stream);
 hipError_t launch_decompress_out(const uint64_t* bits, const float* scales, int64_t L,
                                  int64_t offset, int64_t count, float* dst, hipStream_t stream);
+hipError_t launch_zo_local_model(const float* x, const float* a, const float* v, float gamma,
+                                float eps, int64_t offset, int64_t count, float* dst,
+                                hipStream_t stream);
 
 }  // namespace ob

@@ -381,6 +381,162 @@ __global__ void __launch_bounds__(kBlock)
   }
 }
 
+// ------------------------------------------------------------ 0/1 Adam --
+// "Maximizing Communication Efficiency for Large-scale Training via 0/1
+// Adam" (abstract): local momentum steps with a stale variance, their
+// step-weighted mean momentum sent through the same 1-bit codec at a
+// synchronization.  Per worker and element, a local step is
+//   m_i = (b1*m_src) + ((1-b1)*g_i),   m_src = shared m at the first step of
+//                                      a period, m_i afterwards;
+//   a_i = m_i at the first step, a_i + (w*(m_i - a_i)) afterwards, w = lr/G
+//         (G = the period's summed step sizes, formed on the host);
+// a synchronizing step then forms c = a_i + e_i and compresses it exactly as
+// the worker pass does.  Same mapping as the worker pass (one wave per
+// segment of a (worker, chunk) row, grid.y = worker * n + chunk).
+
+template <typename GT, bool FIRST, bool MBITS>
+__device__ __forceinline__ void zo_momentum(const GT* __restrict__ g, const float* __restrict__ m,
+                                            const float* __restrict__ mloc,
+                                            const float* __restrict__ aloc, uint64_t mword,
+                                            float ms, int64_t k, float beta1, float ob1, float wk,
+                                            float& mi, float& ai) {
+  const float gv = grad_value(g, k);
+  const float msrc = FIRST ? (MBITS ? signed_scale(mword, ms) : m[k]) : ld_stream(mloc + k);
+  mi = (beta1 * msrc) + (ob1 * gv);
+  if (FIRST) {
+    ai = mi;
+  } else {
+    const float ap = ld_stream(aloc + k);
+    ai = ap + (wk * (mi - ap));
+  }
+}
+
+// A local step (no synchronization): stores m_i and a_i.
+template <typename GT, bool FIRST, bool MBITS>
+__global__ void __launch_bounds__(kBlock)
+    zo_local_kernel(GradPtrs g, int64_t d, int64_t L, int n, int64_t nseg,
+                    const float* __restrict__ m, const uint64_t* __restrict__ sbits,
+                    const float* __restrict__ sscale, float* __restrict__ mlocbuf,
+                    float* __restrict__ alocbuf, float beta1, float ob1, float wk) {
+  const int lane = threadIdx.x & 63;
+  const int wi = (int)blockIdx.y / n;
+  const int j = (int)blockIdx.y - wi * n;
+  const GT* __restrict__ gp = (const GT*)g.p[wi];
+  float* __restrict__ mloc = mlocbuf + (int64_t)wi * d;
+  float* __restrict__ aloc = alocbuf + (int64_t)wi * d;
+  const float ms = MBITS ? sscale[j] : 0.0f;
+  const int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
+  if (s >= nseg) return;
+  const int64_t q0 = s * kSegElems;
+  const int64_t left = (L - q0) >> 6;
+  const int rows = left < kSegRows ? (int)left : kSegRows;
+  const int64_t base = (int64_t)j * L + q0;
+  const int64_t wbase = base >> 6;
+  if (rows == kSegRows) {
+#pragma unroll
+    for (int r = 0; r < kSegRows; ++r) {
+      const int64_t k = base + 64 * r + lane;
+      float mi, ai;
+      zo_momentum<GT, FIRST, MBITS>(gp, m, mloc, aloc, MBITS ? sbits[wbase + r] : 0, ms, k,
+                                    beta1, ob1, wk, mi, ai);
+      st_stream(mloc + k, mi);
+      st_stream(aloc + k, ai);
+    }
+  } else {
+    for (int r = 0; r < rows; ++r) {
+      const int64_t k = base + 64 * r + lane;
+      float mi, ai;
+      zo_momentum<GT, FIRST, MBITS>(gp, m, mloc, aloc, MBITS ? sbits[wbase + r] : 0, ms, k,
+                                    beta1, ob1, wk, mi, ai);
+      st_stream(mloc + k, mi);
+      st_stream(aloc + k, ai);
+    }
+  }
+}
+
+// A synchronizing step's worker pass: the local step's a_i (not stored: the
+// period ends), then c = a_i + e with e = c_prev - (c_prev >= 0 ? s_prev :
+// -s_prev), stored with its sign words and the block's partial of the sum of
+// squares, as in worker_kernel.
+template <typename GT, bool FIRST, bool MBITS>
+__global__ void __launch_bounds__(kBlock)
+    zo_sync_kernel(GradPtrs g, int64_t d, int64_t L, int n, int64_t nseg, int64_t words,
+                   const float* __restrict__ m, const uint64_t* __restrict__ sbits,
+                   const float* __restrict__ sscale, const float* __restrict__ mlocbuf,
+                   const float* __restrict__ alocbuf, float* __restrict__ cbuf,
+                   const float* __restrict__ wscale, uint64_t* __restrict__ wbits,
+                   double* __restrict__ wpart, float beta1, float ob1, float wk) {
+  __shared__ double quad_part[kWavesPerBlock];
+  const int lane = threadIdx.x & 63;
+  const int wv = wave_in_block();
+  const int w = (int)blockIdx.y / n;
+  const int j = (int)blockIdx.y - w * n;
+  const GT* __restrict__ gp = (const GT*)g.p[w];
+  const float* __restrict__ mloc = mlocbuf + (int64_t)w * d;
+  const float* __restrict__ aloc = alocbuf + (int64_t)w * d;
+  float* __restrict__ c = cbuf + (int64_t)w * d;
+  uint64_t* __restrict__ bits = wbits + (int64_t)w * words;
+  const int64_t nquad = quads(nseg);
+  double* __restrict__ part = wpart + ((int64_t)w * n + j) * nquad;
+  const float sp = wscale[w * n + j];  // this worker's scale of chunk j at the last sync
+  const float ms = MBITS ? sscale[j] : 0.0f;
+  const int64_t qd = blockIdx.x;  // one quad per block (grid.x == nquad)
+  const int64_t s = qd * kWavesPerBlock + wv;
+  double acc = 0.0;
+  if (s < nseg) {
+    const int64_t q0 = s * kSegElems;
+    const int64_t left = (L - q0) >> 6;
+    const int rows = left < kSegRows ? (int)left : kSegRows;
+    const int64_t base = (int64_t)j * L + q0;
+    const int64_t wbase = base >> 6;
+    uint64_t mine = 0;
+    auto row = [&](int r) {
+      const int64_t k = base + 64 * r + lane;
+      float mi, ai;
+      zo_momentum<GT, FIRST, MBITS>(gp, m, mloc, aloc, MBITS ? sbits[wbase + r] : 0, ms, k,
+                                    beta1, ob1, wk, mi, ai);
+      const float cp = ld_stream(c + k);
+      const float cv = ai + (cp - (cp >= 0.0f ? sp : -sp));
+      st_stream(c + k, cv);
+      const uint64_t word = __ballot(cv >= 0.0f);
+      mine = lane == r ? word : mine;
+      acc = add_square(acc, cv);
+    };
+    if (rows == kSegRows) {
+#pragma unroll
+      for (int r = 0; r < kSegRows; ++r) row(r);
+    } else {
+      for (int r = 0; r < rows; ++r) row(r);
+    }
+    acc = butterfly(acc);
+    if (lane < rows) bits[wbase + lane] = mine;
+  }
+  store_quad_partial(acc, quad_part, part + qd);
+}
+
+// Variance refresh at a synchronization (after the update, which used the
+// stale variance): v = (b2*v) + ((1-b2)*(gbar*gbar)), gbar the pairwise
+// worker average of this step's gradients (as in the warm-up).
+template <typename GT, int NW>
+__global__ void __launch_bounds__(kBlock)
+    zo_refresh_kernel(GradPtrs g, int n, int64_t d, float* __restrict__ v, float beta2,
+                      float ob2) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < d; k += stride) {
+    float sum;
+    if constexpr (NW > 0) {
+      float vals[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) vals[w] = grad_value((const GT*)g.p[w], k);
+      sum = pairwise_sum<NW>(vals);
+    } else {
+      sum = pairwise_sum_stream(n, [&](int w) { return grad_value((const GT*)g.p[w], k); });
+    }
+    const float gbar = sum / (float)(NW > 0 ? NW : n);
+    v[k] = (beta2 * v[k]) + (ob2 * (gbar * gbar));
+  }
+}
+
 // ---------------------------------------------------------- scale finalize --
 // The pairwise sum over a row's segment partials (padded with zeros to a
 // power of two, width W) is split at aligned subtrees of kGroup = 512
@@ -875,6 +1031,18 @@ __global__ void __launch_bounds__(kBlock)
   }
 }
 
+// A worker's local model inside an open 0/1 period: x_sync - G*(a/(sqrtf(v)+eps)).
+__global__ void __launch_bounds__(kBlock)
+    zo_local_model_kernel(const float* __restrict__ x, const float* __restrict__ a,
+                          const float* __restrict__ v, float gamma, float eps, int64_t offset,
+                          int64_t count, float* __restrict__ dst) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < count; i += stride) {
+    const int64_t k = offset + i;
+    dst[i] = x[k] - gamma * (a[k] / (sqrtf(v[k]) + eps));
+  }
+}
+
 // Every launch goes through the runtime's extended launch so that timing
 // events, when requested, are taken from the dispatch packet itself (no extra
 // packets between kernels); with null events it is a plain launch.
@@ -896,7 +1064,7 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 }  // namespace
 
-Layout layout_for(int64_t d, int n) {
+Layout layout_for(int64_t d, int n, bool zero_one) {
   Layout l{};
   const uint64_t ud = (uint64_t)d, un = (uint64_t)n;
   const uint64_t nseg = (uint64_t)((d / n + kSegElems - 1) / kSegElems);
@@ -920,6 +1088,8 @@ Layout layout_for(int64_t d, int n) {
   l.fold = take(8 * un * un * (uint64_t)fold_doubles_per_row((int64_t)nseg));
   l.wscale = take(4 * un * un);
   l.sscale = take(4 * un);
+  l.mloc = take(zero_one ? 4 * ud * un : 0);
+  l.aloc = take(zero_one ? 4 * ud * un : 0);
   l.total = off;
   return l;
 }
@@ -1014,6 +1184,70 @@ hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw,
   if (m_bits) OB_WORK(float, true);
   OB_WORK(float, false);
 #undef OB_WORK
+}
+
+hipError_t launch_zo_local(const State& s, const GradPtrs& g, bool first, bool m_bits, float wk,
+                           hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const float ob1 = 1.0f - s.beta1;
+  const dim3 grid(grid_for(s.nseg, kWavesPerBlock, kMaxBlocksPerRow), (unsigned)(s.n * s.n));
+#define OB_ZOL(GT, F, MB)                                                                       \
+  return launch(zo_local_kernel<GT, F, MB>, grid, dim3(kBlock), stream, t0, t1, g, s.d, s.L, s.n, \
+                s.nseg, (const float*)s.m, (const uint64_t*)s.sbits, (const float*)s.sscale,      \
+                s.mloc, s.aloc, s.beta1, ob1, wk)
+  if (s.grad_bf16) {
+    if (!first) OB_ZOL(uint16_t, false, false);
+    if (m_bits) OB_ZOL(uint16_t, true, true);
+    OB_ZOL(uint16_t, true, false);
+  }
+  if (!first) OB_ZOL(float, false, false);
+  if (m_bits) OB_ZOL(float, true, true);
+  OB_ZOL(float, true, false);
+#undef OB_ZOL
+}
+
+hipError_t launch_zo_sync(const State& s, const GradPtrs& g, bool first, bool m_bits, float wk,
+                          hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const float ob1 = 1.0f - s.beta1;
+  const dim3 grid(grid_for(s.nseg, kWavesPerBlock, kMaxBlocksPerRow), (unsigned)(s.n * s.n));
+#define OB_ZOS(GT, F, MB)                                                                      \
+  return launch(zo_sync_kernel<GT, F, MB>, grid, dim3(kBlock), stream, t0, t1, g, s.d, s.L, s.n, \
+                s.nseg, s.words, (const float*)s.m, (const uint64_t*)s.sbits,                    \
+                (const float*)s.sscale, (const float*)s.mloc, (const float*)s.aloc, s.c,         \
+                (const float*)s.wscale, s.wbits, s.wpart, s.beta1, ob1, wk)
+  if (s.grad_bf16) {
+    if (!first) OB_ZOS(uint16_t, false, false);
+    if (m_bits) OB_ZOS(uint16_t, true, true);
+    OB_ZOS(uint16_t, true, false);
+  }
+  if (!first) OB_ZOS(float, false, false);
+  if (m_bits) OB_ZOS(float, true, true);
+  OB_ZOS(float, true, false);
+#undef OB_ZOS
+}
+
+hipError_t launch_zo_refresh(const State& s, const GradPtrs& g, hipStream_t stream,
+                             hipEvent_t t0, hipEvent_t t1) {
+  const float ob2 = 1.0f - s.beta2;
+  const dim3 grid(grid_for(s.d, kBlock, 8192));
+#define OB_ZOR(GT, NW)                                                                         \
+  return launch(zo_refresh_kernel<GT, NW>, grid, dim3(kBlock), stream, t0, t1, g, s.n, s.d, s.v, \
+                s.beta2, ob2)
+#define OB_ZOR_N(GT)          \
+  switch (s.n) {              \
+    case 1: OB_ZOR(GT, 1);    \
+    case 2: OB_ZOR(GT, 2);    \
+    case 4: OB_ZOR(GT, 4);    \
+    case 8: OB_ZOR(GT, 8);    \
+    case 16: OB_ZOR(GT, 16);  \
+    default: OB_ZOR(GT, 0);   \
+  }
+  if (s.grad_bf16) {
+    OB_ZOR_N(uint16_t)
+  } else {
+    OB_ZOR_N(float)
+  }
+#undef OB_ZOR_N
+#undef OB_ZOR
 }
 
 // Scales of `rows` rows of partials (`nseg` per row: one per segment, or one
@@ -1115,6 +1349,14 @@ hipError_t launch_error_out(const float* comp, const float* scales, int64_t L, i
   if (count <= 0) return hipSuccess;
   return launch(error_out_kernel, dim3(grid_for(count, kBlock, 16384)), dim3(kBlock), stream,
                 nullptr, nullptr, comp, scales, L, offset, count, dst);
+}
+
+hipError_t launch_zo_local_model(const float* x, const float* a, const float* v, float gamma,
+                                float eps, int64_t offset, int64_t count, float* dst,
+                                hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  return launch(zo_local_model_kernel, dim3(grid_for(count, kBlock, 16384)), dim3(kBlock), stream,
+                nullptr, nullptr, x, a, v, gamma, eps, offset, count, dst);
 }
 
 hipError_t launch_decompress_out(const uint64_t* bits, const float* scales, int64_t L,

@@ -18,17 +18,20 @@ LIB_PATH = os.path.join(_PKG, "libob_adam.so")
  OB_ERR_TOO_LARGE) = range(7)
 OB_GRAD_F32, OB_GRAD_BF16 = 0, 1
 (OB_X, OB_M, OB_V, OB_E_WORKER, OB_E_SERVER, OB_BITS_WORKER, OB_BITS_SERVER, OB_SCALE_WORKER,
- OB_SCALE_SERVER) = range(9)
+ OB_SCALE_SERVER, OB_M_LOCAL, OB_A_LOCAL, OB_X_LOCAL) = range(12)
+OB_METHOD_ONE_BIT, OB_METHOD_ZERO_ONE = 0, 1
+OB_ZO_SYNC, OB_ZO_REFRESH = 1, 2
 
 EXPORTED = ("ob_adam_workspace_bytes", "ob_adam_init", "ob_adam_warmup_step",
             "ob_adam_warmup_worker", "ob_adam_warmup_finish",
-            "ob_adam_compressed_step", "ob_adam_compressed_step_static",
+            "ob_adam_compressed_step", "ob_adam_compressed_step_static", "ob_adam_zero_one_step",
             "ob_adam_compress_worker", "ob_adam_compressed_finish",
             "ob_adam_get_state", "ob_adam_set_state", "ob_adam_params", "ob_adam_step_count",
             "ob_adam_get_counters", "ob_adam_attach", "ob_adam_check_guards", "ob_adam_set_debug",
             "ob_adam_set_timing",
             "ob_adam_kernel_times", "ob_adam_destroy", "ob_status_str")
-KERNELS = ("warmup", "worker", "worker_scale", "server", "server_scale", "update")
+KERNELS = ("warmup", "worker", "worker_scale", "server", "server_scale", "update", "zo_local",
+           "zo_refresh")
 
 
 class ObAdamError(RuntimeError):
@@ -40,7 +43,7 @@ class ObAdamError(RuntimeError):
 class ob_adam_config(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int64), ("n_workers", ctypes.c_int32),
                 ("grad_dtype", ctypes.c_int32), ("beta1", ctypes.c_float),
-                ("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
+                ("beta2", ctypes.c_float), ("eps", ctypes.c_float), ("method", ctypes.c_int32)]
 
 
 class ob_adam_counters(ctypes.Structure):
@@ -60,6 +63,7 @@ def _load(path=LIB_PATH):
         "ob_adam_warmup_step": [P, ctypes.POINTER(P), F],
         "ob_adam_compressed_step": [P, ctypes.POINTER(P), F],
         "ob_adam_compressed_step_static": [P, ctypes.POINTER(P), F],
+        "ob_adam_zero_one_step": [P, ctypes.POINTER(P), F, I32],
         "ob_adam_warmup_worker": [P, I32, P],
         "ob_adam_warmup_finish": [P, F],
         "ob_adam_compress_worker": [P, I32, P],
@@ -98,8 +102,9 @@ def ob_status_str(status):
     return _lib.ob_status_str(status).decode()
 
 
-def make_config(d, n_workers, grad_dtype=OB_GRAD_F32, beta1=0.9, beta2=0.999, eps=1e-8):
-    return ob_adam_config(d, n_workers, grad_dtype, beta1, beta2, eps)
+def make_config(d, n_workers, grad_dtype=OB_GRAD_F32, beta1=0.9, beta2=0.999, eps=1e-8,
+                method=OB_METHOD_ONE_BIT):
+    return ob_adam_config(d, n_workers, grad_dtype, beta1, beta2, eps, method)
 
 
 def ob_adam_workspace_bytes(cfg):
@@ -139,6 +144,11 @@ def ob_adam_compressed_step(h, grad_ptrs, lr):
 def ob_adam_compressed_step_static(h, grad_ptrs, lr):
     _check(_lib.ob_adam_compressed_step_static(h, _ptr_array(grad_ptrs), lr),
            "ob_adam_compressed_step_static")
+
+
+def ob_adam_zero_one_step(h, grad_ptrs, lr, flags):
+    _check(_lib.ob_adam_zero_one_step(h, _ptr_array(grad_ptrs), lr, flags),
+           "ob_adam_zero_one_step")
 
 
 def ob_adam_compress_worker(h, worker, grad_ptr):
@@ -217,18 +227,22 @@ def ob_adam_destroy(h):
 _FIELD_DTYPE = {OB_X: torch.float32, OB_M: torch.float32, OB_V: torch.float32,
                 OB_E_WORKER: torch.float32, OB_E_SERVER: torch.float32,
                 OB_BITS_WORKER: torch.int64, OB_BITS_SERVER: torch.int64,
-                OB_SCALE_WORKER: torch.float32, OB_SCALE_SERVER: torch.float32}
+                OB_SCALE_WORKER: torch.float32, OB_SCALE_SERVER: torch.float32,
+                OB_M_LOCAL: torch.float32, OB_A_LOCAL: torch.float32, OB_X_LOCAL: torch.float32}
 
 
 class OneBitAdam:
     """A handle plus the torch-allocated workspace it lives in."""
 
     def __init__(self, d, n_workers, grad_dtype=OB_GRAD_F32, beta1=0.9, beta2=0.999, eps=1e-8,
-                 x0=None, device="cuda", stream=None, checkpoint=None):
+                 x0=None, device="cuda", stream=None, checkpoint=None,
+                 method=OB_METHOD_ONE_BIT):
         """checkpoint: (workspace bytes as a uint8 tensor, counters) from
         checkpoint() of a handle with the same configuration; the state is
-        copied into a fresh workspace and attached instead of initialized."""
-        self.cfg = make_config(d, n_workers, grad_dtype, beta1, beta2, eps)
+        copied into a fresh workspace and attached instead of initialized.
+        method: OB_METHOD_ONE_BIT (compressed_step) or OB_METHOD_ZERO_ONE
+        (zero_one_step)."""
+        self.cfg = make_config(d, n_workers, grad_dtype, beta1, beta2, eps, method)
         self.d, self.n = d, n_workers
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
@@ -309,6 +323,15 @@ class OneBitAdam:
         ptrs = self._grad_ptrs(grads)
         self._order_after_caller(*grads)
         ob_adam_compressed_step_static(self.h, ptrs, lr)
+        self._order_caller_after()
+
+    def zero_one_step(self, grads, lr, sync, refresh=False):
+        """One 0/1 Adam step; `sync` closes the local period, `refresh` (only
+        with sync) refreshes the stale variance."""
+        ptrs = self._grad_ptrs(grads)
+        self._order_after_caller(*grads)
+        ob_adam_zero_one_step(self.h, ptrs, lr,
+                              (OB_ZO_SYNC if sync else 0) | (OB_ZO_REFRESH if refresh else 0))
         self._order_caller_after()
 
     def compress_worker(self, worker, grad):

@@ -85,6 +85,10 @@ typedef enum {
 /* Gradient element types. */
 enum { OB_GRAD_F32 = 0, OB_GRAD_BF16 = 1 };
 
+/* Compression-phase method of a handle: 1-bit Adam (ob_adam_compressed_step
+ * and its variants) or the 0/1 Adam variant (ob_adam_zero_one_step). */
+enum { OB_METHOD_ONE_BIT = 0, OB_METHOD_ZERO_ONE = 1 };
+
 typedef struct {
   int64_t d;          /* parameters; 0 < d <= 2^40, d % (64*n_workers) == 0 and
                          d / n_workers <= 2^30 (chunk length; <= 2^28 for 32
@@ -92,6 +96,9 @@ typedef struct {
   int32_t n_workers;  /* simulated workers; 1 <= n_workers <= 64 */
   int32_t grad_dtype; /* OB_GRAD_F32 or OB_GRAD_BF16 (bf16 is widened exactly) */
   float beta1, beta2, eps;
+  int32_t method;     /* OB_METHOD_ONE_BIT (0, also what a zero-filled or
+                         six-member initializer gives) or OB_METHOD_ZERO_ONE,
+                         which reserves two more fp32 slabs per worker */
 } ob_adam_config;
 
 /* Fields for ob_adam_get_state / ob_adam_set_state. */
@@ -104,7 +111,14 @@ enum {
   OB_BITS_WORKER = 5,  /* uint64[d/64] last sign words of worker `worker` */
   OB_BITS_SERVER = 6,  /* uint64[d/64] last server sign words */
   OB_SCALE_WORKER = 7, /* fp32[n] last scales of worker `worker`, one per chunk */
-  OB_SCALE_SERVER = 8  /* fp32[n] last server scales, one per chunk */
+  OB_SCALE_SERVER = 8, /* fp32[n] last server scales, one per chunk */
+  /* 0/1 Adam handles only (OB_ERR_ARG otherwise): */
+  OB_M_LOCAL = 9,      /* fp32[d] local momentum of worker `worker` in the open
+                          local period (OB_ERR_PHASE right after a sync) */
+  OB_A_LOCAL = 10,     /* fp32[d] its step-size-weighted mean momentum over the
+                          period (OB_ERR_PHASE right after a sync) */
+  OB_X_LOCAL = 11      /* fp32[d] its local model: x - G*(a/(sqrtf(v)+eps)) with G
+                          the period's summed step sizes; x right after a sync */
 };
 
 /* Bytes of device workspace a configuration needs (256-byte aligned start). */
@@ -175,6 +189,33 @@ ob_status ob_adam_compressed_step(ob_adam_t h, const void* const* grads, float l
  * array: order them (one stream, or events). */
 ob_status ob_adam_compressed_step_static(ob_adam_t h, const void* const* grads, float lr);
 
+/* One step of the 0/1 Adam variant ("Maximizing Communication Efficiency for
+ * Large-scale Training via 0/1 Adam", abstract: each Adam step is made
+ * linear by stale state estimates and the linear correlation of momentum and
+ * update, so 1-bit compression and local steps combine), for handles made
+ * with method OB_METHOD_ZERO_ONE, in the compression phase (after at least
+ * one warm-up step; OB_ERR_PHASE otherwise, and for 1-bit handles).
+ * Per worker i and element (fp32, in this order):
+ *  - G = lr at the first step of a local period, G + lr after; w = lr / G;
+ *  - m_i = (b1*m_src) + ((1-b1)*g_i), m_src = the shared momentum at the
+ *    period's first step, m_i after;
+ *  - a_i = m_i at the first step, a_i + (w*(m_i - a_i)) after (the
+ *    step-weighted mean momentum; the worker's local model is
+ *    x - G*(a_i/(sqrtf(v)+eps)), linear in its gradients while v is stale).
+ * flags & OB_ZO_SYNC closes the period: c_i = a_i + e_i goes through the
+ * compressed step's codec (per-chunk scale, sign words, worker error; server
+ * average, server error, server scale and words), the decompressed server
+ * output becomes the shared momentum m, and x = x - G*(m/(sqrtf(v)+eps)).
+ * flags & OB_ZO_REFRESH (only with OB_ZO_SYNC; OB_ERR_ARG otherwise) then
+ * refreshes the stale variance: v = (b2*v) + ((1-b2)*(gbar*gbar)), gbar the
+ * pairwise worker average of this step's gradients as in the warm-up.
+ * With OB_ZO_SYNC at every step and no refresh the result equals
+ * ob_adam_compressed_step's bit for bit.  grads as for that call.  The
+ * schedule of synchronizations and refreshes is the caller's.  Counters
+ * (ob_adam_get_counters) can be taken only between local periods. */
+enum { OB_ZO_SYNC = 1, OB_ZO_REFRESH = 2 };
+ob_status ob_adam_zero_one_step(ob_adam_t h, const void* const* grads, float lr, int32_t flags);
+
 /* The same step with the gradients supplied one worker at a time, so that a
  * caller can regenerate each worker's gradient into one buffer (bounded
  * memory).  Call ob_adam_compress_worker once for every worker w (any order;
@@ -234,7 +275,8 @@ typedef struct {
   int64_t warmup_steps;     /* warm-up steps taken */
 } ob_adam_counters;
 
-/* OB_ERR_PHASE while a worker-at-a-time step (warm-up or compressed) is open. */
+/* OB_ERR_PHASE while a worker-at-a-time step (warm-up or compressed) or a
+ * 0/1 Adam local period is open. */
 ob_status ob_adam_get_counters(ob_adam_t h, ob_adam_counters* out);
 
 /* Like ob_adam_init, but adopts a workspace that already holds a state
@@ -251,7 +293,8 @@ ob_status ob_adam_attach(const ob_adam_config* cfg, void* workspace, uint64_t ws
  * *first_bad to -1 when all are intact, else to the index (in workspace
  * order: x, m, v, u, worker compensated slabs, worker sign words, server sign
  * words, worker partials, server partials, fold buffer, worker scales, server
- * scales) of the first guard found changed -- a write past that buffer's
+ * scales, 0/1 local momenta, 0/1 mean momenta -- the last two empty for
+ * 1-bit handles) of the first guard found changed -- a write past that buffer's
  * end.  A workspace adopted by ob_adam_attach keeps the guards of the copy. */
 ob_status ob_adam_check_guards(ob_adam_t h, int32_t* first_bad);
 
@@ -279,7 +322,9 @@ enum {
   OB_K_SERVER = 3,        /* server average / re-compress pass */
   OB_K_SERVER_SCALE = 4,  /* server scale finalize */
   OB_K_UPDATE = 5,        /* decompress + frozen-variance update */
-  OB_NUM_KERNELS = 6
+  OB_K_ZO_LOCAL = 6,      /* 0/1 Adam local step (a sync step's worker pass is OB_K_WORKER) */
+  OB_K_ZO_REFRESH = 7,    /* 0/1 Adam variance refresh */
+  OB_NUM_KERNELS = 8
 };
 
 /* Per-kernel timing.  With max_launches > 0, each later kernel launch (for a

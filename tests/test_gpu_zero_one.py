@@ -1,0 +1,199 @@
+"""Parity of the 0/1 Adam step's HIP path (ob_adam_zero_one_step, through
+the C interface) with the CPU oracle's ob_oracle_zo_step, and its reduction
+to the 1-bit Adam step.
+
+Every field is compared with the oracle after every step, bit for bit: the
+shared x, m and v, the worker and server errors, sign words and scales, and
+while a local period is open every worker's local momentum, step-weighted
+mean momentum and local model.  Schedules mix local steps, synchronizations
+and variance refreshes with changing step sizes; worker counts cover every
+server form (1, 3, 4, 5, 8, 16, 64), bf16 and fp32 gradients, chunks with a
+ragged last segment.  With a synchronization at every step and no refresh
+the HIP 0/1 step must equal the HIP 1-bit compressed step bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_common import compare_full, gpu_np, host_grads, log, to_device_grad
+
+pytestmark = pytest.mark.gpu
+
+ob = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global ob
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from communication_compressed_distributed_02_amd import ob_adam
+    ob = ob_adam
+
+
+L, S, R = "local", "sync", "sync+refresh"
+
+SCHEDULES = {
+    "every_step": [S] * 5,
+    "pairs_refresh_doubling": [L, R, L, R, L, S, L, R],
+    "triples": [L, L, S, L, L, R, L, L, S],
+    "irregular": [L, L, L, R, S, L, S, L, L, L, L, S],
+}
+
+CASES = [
+    # (name, d, n, bf16, warm, schedule)
+    ("n4_ragged_pairs", 4 * 3392, 4, False, 2, "pairs_refresh_doubling"),
+    ("n3_generic_triples", 3 * 1472, 3, False, 1, "triples"),
+    ("n1_irregular", 2112, 1, False, 1, "irregular"),
+    ("n8_bf16_irregular", 8 * 2112, 8, True, 2, "irregular"),
+    ("n5_generic_pairs", 5 * 1088, 5, False, 1, "pairs_refresh_doubling"),
+    ("n16_triples", 16 * 1152, 16, False, 1, "triples"),
+    ("n64_pairs", 64 * 1088, 64, False, 1, "pairs_refresh_doubling"),
+    ("n8_every_step", 8 * 2112, 8, True, 2, "every_step"),
+]
+
+
+def lr_at(t):
+    return np.float32(1e-3 * (1.0 + 0.3 * ((7 * t) % 5)))  # changes every step
+
+
+def compare_local(opt, orc, n, where):
+    for w in range(n):
+        for name, gf, of in (("m_local", ob.OB_M_LOCAL, oracle.M_LOCAL),
+                             ("a_local", ob.OB_A_LOCAL, oracle.A_LOCAL),
+                             ("x_local", ob.OB_X_LOCAL, oracle.X_LOCAL)):
+            g = gpu_np(opt, gf, w).view(np.uint32)
+            r = orc.get(of, w).view(np.uint32)
+            if not np.array_equal(g, r):
+                i = int(np.flatnonzero(g != r)[0])
+                raise AssertionError("%s worker %d %s differs at %d: %r vs %r" % (
+                    where, w, name, i, g[i:i + 1].view(np.float32)[0],
+                    r[i:i + 1].view(np.float32)[0]))
+
+
+@pytest.mark.parametrize("name,d,n,bf16,warm,sched", CASES, ids=[c[0] for c in CASES])
+def test_zero_one_matches_oracle(name, d, n, bf16, warm, sched):
+    import torch
+    plan = SCHEDULES[sched]
+    log("case %s: d=%d n=%d bf16=%s warm=%d schedule=%s" % (name, d, n, bf16, warm, plan))
+    opt = ob.OneBitAdam(d, n, ob.OB_GRAD_BF16 if bf16 else ob.OB_GRAD_F32,
+                        method=ob.OB_METHOD_ZERO_ONE)
+    orc = oracle.Oracle(d, n)
+    sigma = 1e-3 if bf16 else 1e-2
+    for t in range(warm + len(plan)):
+        hg = host_grads(d, n, t, sigma=sigma, bf16=bf16)
+        dg = [to_device_grad(g) for g in hg]
+        lr = lr_at(t)
+        if t < warm:
+            opt.warmup_step(dg, lr)
+            orc.warmup_step(hg, lr)
+            continue
+        kind = plan[t - warm]
+        opt.zero_one_step(dg, lr, sync=kind != L, refresh=kind == R)
+        orc.zo_step(hg, lr, sync=kind != L, refresh=kind == R)
+        torch.cuda.synchronize()
+        where = "%s step %d (%s)" % (name, t, kind)
+        compare_full(opt, orc, True, exact=True, where=where)
+        if kind == L:
+            assert orc.zo_open > 0
+            compare_local(opt, orc, n, where)
+        else:
+            with pytest.raises(ob.ObAdamError) as e:
+                opt.get(ob.OB_M_LOCAL, 0)
+            assert e.value.status == ob.OB_ERR_PHASE
+            np.testing.assert_array_equal(gpu_np(opt, ob.OB_X_LOCAL, n - 1), gpu_np(opt, ob.OB_X))
+    assert opt.check_guards() == -1, "a kernel wrote past the end of a workspace buffer"
+
+
+@pytest.mark.parametrize("n,bf16", [(4, False), (8, True), (3, False)])
+def test_sync_every_step_equals_the_compressed_step_on_the_gpu(n, bf16):
+    """Two GPU handles fed the same gradients: 0/1 steps with a
+    synchronization every step and no refresh, and 1-bit compressed steps.
+    Every field identical after every step."""
+    import torch
+    d = n * 3392
+    a = ob.OneBitAdam(d, n, ob.OB_GRAD_BF16 if bf16 else ob.OB_GRAD_F32)
+    b = ob.OneBitAdam(d, n, ob.OB_GRAD_BF16 if bf16 else ob.OB_GRAD_F32,
+                      method=ob.OB_METHOD_ZERO_ONE)
+    for t in range(2 + 6):
+        dg = [to_device_grad(g) for g in host_grads(d, n, t, sigma=1e-3 if bf16 else 1e-2,
+                                                    bf16=bf16)]
+        lr = lr_at(t)
+        if t < 2:
+            a.warmup_step(dg, lr)
+            b.warmup_step(dg, lr)
+            continue
+        a.compressed_step(dg, lr)
+        b.zero_one_step(dg, lr, sync=True)
+        torch.cuda.synchronize()
+        fields = [(ob.OB_X, 0), (ob.OB_M, 0), (ob.OB_V, 0), (ob.OB_E_SERVER, 0),
+                  (ob.OB_BITS_SERVER, 0), (ob.OB_SCALE_SERVER, 0)]
+        fields += [(f, w) for w in range(n)
+                   for f in (ob.OB_E_WORKER, ob.OB_BITS_WORKER, ob.OB_SCALE_WORKER)]
+        for f, w in fields:
+            assert torch.equal(a.get(f, w), b.get(f, w)), (t, f, w)
+
+
+def test_phase_and_flag_rules():
+    """A 1-bit handle refuses 0/1 steps and a 0/1 handle compressed steps;
+    refresh needs a sync; counters only between local periods; the local
+    fields belong to 0/1 handles."""
+    d, n = 4 * 1088, 4
+    dg = [to_device_grad(g) for g in host_grads(d, n, 0)]
+    one = ob.OneBitAdam(d, n)
+    zo = ob.OneBitAdam(d, n, method=ob.OB_METHOD_ZERO_ONE)
+    with pytest.raises(ob.ObAdamError) as e:  # before any warm-up step
+        zo.zero_one_step(dg, 1e-3, sync=True)
+    assert e.value.status == ob.OB_ERR_PHASE
+    with pytest.raises(ob.ObAdamError) as e:
+        one.compressed_step(dg, 1e-3)
+    assert e.value.status == ob.OB_ERR_PHASE
+    one.warmup_step(dg, 1e-3)
+    zo.warmup_step(dg, 1e-3)
+    with pytest.raises(ob.ObAdamError) as e:
+        one.zero_one_step(dg, 1e-3, sync=True)
+    assert e.value.status == ob.OB_ERR_PHASE
+    with pytest.raises(ob.ObAdamError) as e:
+        zo.compressed_step(dg, 1e-3)
+    assert e.value.status == ob.OB_ERR_PHASE
+    with pytest.raises(ob.ObAdamError) as e:
+        zo.compressed_step_static(dg, 1e-3)
+    assert e.value.status == ob.OB_ERR_PHASE
+    with pytest.raises(ob.ObAdamError) as e:
+        zo.zero_one_step(dg, 1e-3, sync=False, refresh=True)
+    assert e.value.status == ob.OB_ERR_ARG
+    with pytest.raises(ob.ObAdamError) as e:
+        ob.ob_adam_zero_one_step(zo.h, [g.data_ptr() for g in dg], 1e-3, 4)
+    assert e.value.status == ob.OB_ERR_ARG
+    with pytest.raises(ob.ObAdamError) as e:
+        one.get(ob.OB_X_LOCAL, 0)
+    assert e.value.status == ob.OB_ERR_ARG
+    zo.zero_one_step(dg, 1e-3, sync=False)
+    with pytest.raises(ob.ObAdamError) as e:
+        ob.ob_adam_get_counters(zo.h)
+    assert e.value.status == ob.OB_ERR_PHASE
+    zo.zero_one_step(dg, 1e-3, sync=True)
+    assert ob.ob_adam_get_counters(zo.h) == (3, 2, 1)
+
+
+def test_checkpoint_resume_between_periods():
+    """A 0/1 run checkpointed right after a synchronization and resumed in a
+    fresh handle continues bit-identically to the uninterrupted run."""
+    import torch
+    d, n = 8 * 1088, 8
+    plan = [L, S, L, L, R, L, S]
+    a = ob.OneBitAdam(d, n, method=ob.OB_METHOD_ZERO_ONE)
+    grads = [[to_device_grad(g) for g in host_grads(d, n, t)] for t in range(1 + len(plan))]
+    a.warmup_step(grads[0], 1e-3)
+    for t, kind in enumerate(plan[:2]):
+        a.zero_one_step(grads[1 + t], lr_at(t), sync=kind != L, refresh=kind == R)
+    ck = a.checkpoint()
+    b = ob.OneBitAdam(d, n, method=ob.OB_METHOD_ZERO_ONE, checkpoint=ck)
+    for t, kind in enumerate(plan[2:], start=2):
+        for h in (a, b):
+            h.zero_one_step(grads[1 + t], lr_at(t), sync=kind != L, refresh=kind == R)
+    torch.cuda.synchronize()
+    for f, w in [(ob.OB_X, 0), (ob.OB_M, 0), (ob.OB_V, 0), (ob.OB_E_SERVER, 0)] + \
+            [(ob.OB_E_WORKER, w) for w in range(n)]:
+        assert torch.equal(a.get(f, w), b.get(f, w)), (f, w)
+    assert a.steps == b.steps
