@@ -96,13 +96,13 @@ int main(int argc, char** argv) {
   const float lr = 1e-3f;
 
   /* error paths: nothing is enqueued, no handle is made */
-  ob_adam_config bad = {d + 1, n, OB_GRAD_F32, 0.9f, 0.999f, 1e-8f};
+  ob_adam_config bad = {d + 1, n, OB_GRAD_F32, 0.9f, 0.999f, 1e-8f, OB_METHOD_ONE_BIT};
   uint64_t bytes = 0;
   check(ob_adam_workspace_bytes(&bad, &bytes) == OB_ERR_SHAPE, "shape rule");
   check(ob_adam_workspace_bytes(NULL, &bytes) == OB_ERR_ARG, "null config");
   check(ob_status_str(OB_ERR_PHASE) != NULL, "status string");
 
-  ob_adam_config cfg = {d, n, OB_GRAD_F32, 0.9f, 0.999f, 1e-8f};
+  ob_adam_config cfg = {d, n, OB_GRAD_F32, 0.9f, 0.999f, 1e-8f, OB_METHOD_ONE_BIT};
   OB_OK_(ob_adam_workspace_bytes(&cfg, &bytes));
   void* ws = NULL;
   HIP_OK(hipMalloc(&ws, bytes));
