@@ -36,6 +36,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "compressed-step params·workers/sec and achieved HBM GB/s (% of peak), 1 GPU"
+# the 0/1 Adam workloads' line: the same units over their steps' mix
+ZO_METRIC = "0/1 Adam step params·workers/sec and achieved HBM GB/s (% of peak), 1 GPU"
 KERNEL_SRC = os.path.join(ROOT, "communication_compressed_distributed_02_amd", "csrc",
                           "ob_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "worker_pass_%s_counters.txt")  # % workload
@@ -69,6 +71,31 @@ def alg_bytes(w):
         "server_scale": part_s + 4 * n,
         # server words in, x in and out, v in
         "update": d // 8 + 12 * d + 4 * n,
+    }
+
+
+def zo_alg_bytes(w):
+    """The 0/1 Adam workloads: algorithmic bytes per launch of each kernel, a
+    schedule with `sync_every` = 2 (every local step opens a period, every
+    synchronizing step closes it).  Local step: gradient in, local momentum
+    and mean momentum out, shared momentum's words in.  Synchronizing worker
+    pass: gradient, local momentum, mean momentum and compensated momentum
+    in, compensated momentum and sign words out, partials.  Refresh: all
+    workers' gradients in, v in and out.  Scales, server pass and update as
+    in the compressed step."""
+    d, n = w.d, w.n
+    gb = 2 if w.bf16 else 4
+    b = alg_bytes(w)
+    nseg = -(-w.L // 1024)
+    part_w = 8 * n * n * -(-nseg // 4)
+    return {
+        "zo_local": n * d * (gb + 8) + d // 8,
+        "worker": n * d * (gb + 4 + 4 + 4 + 4) + n * d // 8 + part_w,
+        "worker_scale": b["worker_scale"],
+        "server": b["server"],
+        "server_scale": b["server_scale"],
+        "update": b["update"],
+        "zo_refresh": n * d * gb + 8 * d,
     }
 
 
@@ -169,9 +196,11 @@ def cpu_baseline(w, steps=1, snap=None):
         "to bound its run)" % (w.warmup, warm))
     return {"value": w.n * w.d / per_step, "unit": "params*workers/s", "cores": 1,
             "kind": "oracle",
-            "sample": "chunk 0 of %d (%d elements x %d workers), %d compressed step(s) after "
+            "sample": "chunk 0 of %d (%d elements x %d workers), %d %s step(s) after "
                       "%d warm-up step(s)%s, single thread pinned to core %d, time x%d for the "
-                      "whole step" % (w.n, L, w.n, steps, warm, short, core, w.n),
+                      "whole step" % (w.n, L, w.n, steps,
+                                      "0/1 Adam" if w.method == "zero_one" else "compressed",
+                                      warm, short, core, w.n),
             "host_cpu": model, "host_cores_usable": usable,
             "s_per_step_extrapolated": per_step}, parity
 
@@ -231,7 +260,11 @@ def _oracle_step_seconds(oracle, W, w, L, warm, steps):
             o.warmup_step(g, w.lr_at(t))
             continue
         t0 = time.perf_counter()
-        o.compressed_step(g, w.lr_at(t))
+        if w.method == "zero_one":
+            sync, refresh = w.zo_flags(w.warmup + t - warm)
+            o.zo_step(g, w.lr_at(t), sync, refresh)
+        else:
+            o.compressed_step(g, w.lr_at(t))
         secs.append(time.perf_counter() - t0)
         del g
     return sum(secs) / len(secs) * w.n, o
@@ -377,15 +410,21 @@ def main():
         ring_grads.append(list(g.unbind(0)))
     grads = [ring_grads[t % ring] for t in range(batches)]
 
+    zero_one = w.method == "zero_one"
+
     def step(opt, t):
-        if w.staged:
+        if zero_one:
+            sync, refresh = w.zo_flags(t)
+            opt.zero_one_step(grads[t], w.lr_at(t), sync, refresh)
+        elif w.staged:
             for i in range(w.n):
                 opt.compress_worker(i, grads[t][i])
             opt.compressed_finish(w.lr_at(t))
         else:
             opt.compressed_step(grads[t], w.lr_at(t))
     opt = ob.OneBitAdam(w.d, w.n, ob.OB_GRAD_BF16 if w.bf16 else ob.OB_GRAD_F32, w.beta1,
-                        w.beta2, w.eps, device=dev)
+                        w.beta2, w.eps, device=dev,
+                        method=ob.OB_METHOD_ZERO_ONE if zero_one else ob.OB_METHOD_ONE_BIT)
     for t in range(w.warmup):
         if w.staged:
             for i in range(w.n):
@@ -433,9 +472,9 @@ def main():
     kt, dropped = ob.ob_adam_kernel_times(opt.h)
     ob.ob_adam_set_timing(opt.h, 0)
 
-    ab = alg_bytes(w)
+    ab = zo_alg_bytes(w) if zero_one else alg_bytes(w)
     kernels = {}
-    for k in ("worker", "worker_scale", "server", "server_scale", "update"):
+    for k in ab:
         ms, cnt = kt[k]
         if cnt:
             avg = ms / cnt
@@ -455,9 +494,24 @@ def main():
     # committed trace of this kernel code (per launch: bytes of one launch)
     per_launch = ab["worker"] // (w.n if w.staged else 1)
     trace_gbs = per_launch / (trace["avg_ns"] * 1e-9) / 1e9 if trace else None
-    step_bytes = sum(ab.values())
+    if zero_one:
+        # mean bytes per step over the timed steps' schedule (local steps,
+        # synchronizing steps with their finalizes, server pass and update,
+        # refreshes where flagged)
+        tot = 0
+        for t in range(w.warmup + a.warmup, w.warmup + a.warmup + a.steps):
+            sync, refresh = w.zo_flags(t)
+            if not sync:
+                tot += ab["zo_local"]
+                continue
+            tot += sum(ab[k] for k in ("worker", "worker_scale", "server", "server_scale",
+                                       "update"))
+            tot += ab["zo_refresh"] if refresh else 0
+        step_bytes = tot / a.steps
+    else:
+        step_bytes = sum(ab.values())
     result = {
-        "metric": METRIC,
+        "metric": ZO_METRIC if zero_one else METRIC,
         "value": w.n * w.d / (ms_step * 1e-3),
         "unit": "params*workers/s",
         "n_gpus": 1,
@@ -471,8 +525,9 @@ def main():
         "data": "synthetic",
         "config": dict(W.describe(w), parallelism="n simulated data-parallel workers on 1 GPU",
                        gradient_batches=ring, entry_point="staged per-worker" if w.staged
-                       else "all workers"),
-        "roofline": {"bound": "hbm", "kernel": "worker pass",
+                       else ("0/1 Adam steps, all workers" if zero_one else "all workers")),
+        "roofline": {"bound": "hbm",
+                     "kernel": "synchronizing worker pass" if zero_one else "worker pass",
                      "achieved": round(wk["GB_s"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(wk["GB_s"] / HBM_PEAK_GBS, 4),
                      "frac_source": "HIP events around every worker-pass launch of timing "
@@ -491,8 +546,8 @@ def main():
                      "launches_per_step": w.n if w.staged else 1},
         "step": {"alg_bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                  "frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "fp32_momentum_bytes": fp32_momentum_step_bytes(w),
-                 "fp32_momentum_frac_of_peak": round(
+                 "fp32_momentum_bytes": None if zero_one else fp32_momentum_step_bytes(w),
+                 "fp32_momentum_frac_of_peak": None if zero_one else round(
                      fp32_momentum_step_bytes(w) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "traffic": traffic.get("step_bytes") if traffic else None,
                  "traffic_GB_s": round(traffic["step_bytes"] / (ms_step * 1e-3) / 1e9, 1)

@@ -1,4 +1,4 @@
-"""The five synthetic workloads the step is checked and measured on.
+"""The synthetic workloads the steps are checked and measured on.
 
 Each stands in for a training job of the kind the pages report on (BERT-Base,
 BERT-Large and GPT-2 pre-training, "1-bit Adam ..." Abstract and the 0/1 Adam
@@ -36,6 +36,8 @@ class Workload:
     pads: list = field(default_factory=list)  # [(start, end)) zero-gradient ranges
     tensors: int = 1
     raw: int = 0                # elements before padding
+    method: str = "one_bit"     # or "zero_one": 0/1 Adam steps after the warm-up
+    sync_every: int = 1         # 0/1 Adam: local steps per synchronization
 
     @property
     def L(self):
@@ -51,6 +53,16 @@ class Workload:
             return np.float32(self.lr)
         T, Tw = self.steps, self.warmup
         return np.float32(self.lr * (T - t) / (T - Tw))
+
+    def zo_flags(self, t):
+        """(sync, refresh) of 0-based step t >= warmup of a 0/1 Adam workload:
+        a synchronization every `sync_every` steps, and a variance refresh at
+        the synchronizations whose count is a power of two (1st, 2nd, 4th,
+        ...: intervals that double)."""
+        k = t - self.warmup + 1
+        sync = k % self.sync_every == 0
+        syncs = k // self.sync_every
+        return sync, sync and (syncs & (syncs - 1)) == 0
 
     def pad_mask(self, lo, hi):
         """Boolean mask over [lo, hi): True where the gradient is forced to 0."""
@@ -129,6 +141,19 @@ def make(name):
         d, pads, raw = _flat(340_000_000, 64)
         return Workload("c5", d=d, n=64, warmup=30, compressed=170, sigma=1e-3,
                         linear_decay=True, staged=True, pads=pads, raw=raw)
+    # 0/1 Adam ("Maximizing Communication Efficiency for Large-scale Training
+    # via 0/1 Adam", abstract: BERT-Base and BERT-Large pre-training among its
+    # benchmarks; about half the communication rounds of 1-bit Adam): a
+    # synchronization every 2 steps
+    if name == "z2":
+        d, pads, raw = _flat(110_000_000, 8)
+        return Workload("z2", d=d, n=8, warmup=2, compressed=20, sigma=1e-3, bf16=True,
+                        pads=pads, raw=raw, method="zero_one", sync_every=2)
+    if name == "z3":
+        sizes = bert_large_sizes()
+        d, pads, raw = _layout(sizes, 16)
+        return Workload("z3", d=d, n=16, warmup=3, compressed=12, sigma=1e-3, pads=pads,
+                        tensors=len(sizes), raw=raw, method="zero_one", sync_every=2)
     if name == "idx64":
         # not a workload of the pages: the largest arrays of the tests, so
         # that element indices run past 2^31 (chunk 3 straddles it)
@@ -138,6 +163,7 @@ def make(name):
 
 
 NAMES = ("c1", "c2", "c3", "c4", "c5")
+ZERO_ONE = ("z2", "z3")  # the 0/1 Adam workloads
 EXTRA = ("idx64",)  # size edge case of the tests
 
 
@@ -145,7 +171,8 @@ def describe(w):
     return {"workload": w.name, "d": w.d, "n_workers": w.n, "chunk": w.L,
             "grads": ("bf16" if w.bf16 else "fp32") + (" student-t3" if w.dist else " normal"),
             "sigma": w.sigma, "warmup_steps": w.warmup, "compressed_steps": w.compressed,
-            "tensors": w.tensors}
+            "tensors": w.tensors, "method": w.method,
+            **({"sync_every": w.sync_every} if w.method == "zero_one" else {})}
 
 
 def cpu_grad(w, worker, step, lo, hi):

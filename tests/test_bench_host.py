@@ -115,3 +115,23 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+@pytest.mark.parametrize("name", ["z2", "z3"])
+def test_zero_one_schedule_and_bytes(name):
+    """0/1 workloads: a synchronization every second step, refreshes at the
+    1st, 2nd, 4th, 8th ... synchronization; the synchronizing worker pass
+    moves gradient + local, mean and compensated momentum in and the
+    compensated momentum out (16 B + gb per element and worker), the local
+    step gradient in and both momenta out (8 B + gb)."""
+    w = W.make(name)
+    flags = [w.zo_flags(t) for t in range(w.warmup, w.warmup + 20)]
+    assert [s for s, _ in flags] == [False, True] * 10
+    refreshed = [k + 1 for k, (s, r) in enumerate([f for f in flags if f[0]]) if r]
+    assert refreshed == [1, 2, 4, 8]
+    gb = 2 if w.bf16 else 4
+    ab = bench.zo_alg_bytes(w)
+    assert ab["zo_local"] == w.n * w.d * (gb + 8) + w.d // 8
+    nquad = -(-(-(-w.L // 1024)) // 4)
+    assert ab["worker"] == w.n * w.d * (gb + 16) + w.n * w.d // 8 + 8 * w.n * w.n * nquad
+    assert ab["zo_refresh"] == w.n * w.d * gb + 8 * w.d
