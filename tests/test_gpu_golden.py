@@ -44,8 +44,11 @@ def load_golden(name):
     for f in sorted(glob.glob(os.path.join(HERE, "golden", name, "chunk_*.json"))):
         with open(f) as fh:
             rec = json.load(fh)
-        with np.load(f[:-len(".json")] + ".npz") as z:  # allow_pickle stays off
-            rec["arrays"] = {k: z[k] for k in z.files}
+        npz = f[:-len(".json")] + ".npz"
+        rec["arrays"] = None
+        if os.path.exists(npz):
+            with np.load(npz) as z:  # allow_pickle stays off
+                rec["arrays"] = {k: z[k] for k in z.files}
         recs.append(rec)
     return recs
 
@@ -113,6 +116,9 @@ def test_full_size_against_stored_oracle(name, front_end):
     recs = load_golden(name)
     if not recs:
         pytest.skip("no stored oracle values for %s" % name)
+    if any(r.get("arrays") is None for r in recs):
+        pytest.skip("stored oracle values for %s predate the 4096-sample format (no .npz): "
+                    "rewrite them with tests/golden/make_golden.py" % name)
     w = W.make(name)
     L, n = w.L, w.n
     wpc = L // 64  # sign words per chunk
@@ -131,10 +137,17 @@ def test_full_size_against_stored_oracle(name, front_end):
         offsets, d = flat_layout(tensor_sizes(name), n)
         assert d == w.d and fe.opt.d == w.d and fe.opt.offsets == offsets
         assert len(fe.params) == w.tensors
-        # every gap between the tensors and the tail is exactly a padding range
+        # the gaps between the tensors and the tail are exactly the padding
+        # (adjacent padding ranges merged)
         ends = [o + k for o, k in zip(offsets, tensor_sizes(name))]
         gaps = [(e, o) for e, o in zip(ends, offsets[1:] + [d]) if o > e]
-        assert gaps == [tuple(p) for p in w.pads]
+        merged = []
+        for lo, hi in w.pads:
+            if merged and merged[-1][1] == lo:
+                merged[-1] = (merged[-1][0], hi)
+            else:
+                merged.append((lo, hi))
+        assert gaps == merged
         opt = fe.core
     else:
         zero_one = w.method == "zero_one"
