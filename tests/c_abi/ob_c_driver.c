@@ -2,7 +2,9 @@
  * memory from hipMalloc, warm-up and compressed steps, the state read back
  * with ob_adam_get_state and compared with the CPU oracle, which is linked
  * in as test infrastructure.  Also checks a few error paths and the
- * workspace guards.
+ * workspace guards.  A second handle with the 0/1 Adam method runs local
+ * steps, synchronizations and a variance refresh; its fields, the open
+ * period's local ones included, must equal the oracle's bit for bit.
  *
  * usage: ob_c_driver d n        exit status 0 = every check passed
  */
@@ -85,6 +87,81 @@ static void compare_bits(ob_adam_t h, ob_oracle* o, int32_t field, int32_t ofiel
   check(memcmp(host, ref, elem * (size_t)count) == 0, what);
 }
 
+/* fresh test gradients for every worker, copied to the device on `stream` */
+static void new_grads(int64_t d, int32_t n, float** hg, void** dg, hipStream_t stream) {
+  for (int w = 0; w < n; ++w) {
+    for (int64_t k = 0; k < d; ++k) hg[w][k] = next_uniform(1e-2f);
+    HIP_OK(hipMemcpyAsync(dg[w], hg[w], sizeof(float) * (size_t)d, hipMemcpyHostToDevice,
+                          stream));
+  }
+}
+
+/* 0/1 Adam: one warm-up step, then local (L), synchronizing (S) and
+ * synchronizing-with-refresh (R) steps with a step size that changes every
+ * step.  While a period is open the local momentum, mean momentum and local
+ * model of every worker are compared; after the last step every shared field. */
+static void run_zero_one(int64_t d, int32_t n, float** hg, void** dg, float* dev, float* host,
+                         hipStream_t stream) {
+  static const char plan[] = "LRLLSLR";
+  const int steps = (int)(sizeof(plan) - 1);
+  ob_adam_config cfg = {d, n, OB_GRAD_F32, 0.9f, 0.999f, 1e-8f, OB_METHOD_ZERO_ONE};
+  uint64_t bytes = 0;
+  OB_OK_(ob_adam_workspace_bytes(&cfg, &bytes));
+  void* ws = NULL;
+  HIP_OK(hipMalloc(&ws, bytes));
+  ob_adam_t h = NULL;
+  OB_OK_(ob_adam_init(&cfg, ws, bytes, NULL, (void*)stream, &h));
+  ob_oracle* o = ob_oracle_create(d, n, 0, n, cfg.beta1, cfg.beta2, cfg.eps, 1);
+  check(o != NULL, "oracle create (0/1)");
+  if (o == NULL) exit(4);
+
+  new_grads(d, n, hg, dg, stream);
+  check(ob_adam_compressed_step(h, (const void* const*)dg, 1e-3f) == OB_ERR_PHASE,
+        "1-bit compressed step on a 0/1 handle");
+  OB_OK_(ob_adam_warmup_step(h, (const void* const*)dg, 1e-3f));
+  ob_oracle_warmup_step(o, (const void* const*)hg, 0, 1e-3f);
+  HIP_OK(hipStreamSynchronize(stream));
+  check(ob_adam_zero_one_step(h, (const void* const*)dg, 1e-3f, OB_ZO_REFRESH) == OB_ERR_ARG,
+        "refresh without a synchronization");
+
+  for (int t = 0; t < steps; ++t) {
+    const float lr = 1e-3f * (1.0f + 0.25f * (float)(t % 3));
+    const int sync = plan[t] != 'L', refresh = plan[t] == 'R';
+    new_grads(d, n, hg, dg, stream);
+    OB_OK_(ob_adam_zero_one_step(h, (const void* const*)dg, lr,
+                                 (sync ? OB_ZO_SYNC : 0) | (refresh ? OB_ZO_REFRESH : 0)));
+    ob_oracle_zo_step(o, (const void* const*)hg, 0, lr, sync, refresh);
+    HIP_OK(hipStreamSynchronize(stream));
+    if (!sync) {
+      check(ob_oracle_zo_open(o) > 0, "oracle period open");
+      for (int w = 0; w < n; ++w) {
+        compare_bits(h, o, OB_M_LOCAL, OBO_M_LOCAL, w, d, 4, dev, host, "0/1 local momentum");
+        compare_bits(h, o, OB_A_LOCAL, OBO_A_LOCAL, w, d, 4, dev, host, "0/1 mean momentum");
+        compare_bits(h, o, OB_X_LOCAL, OBO_X_LOCAL, w, d, 4, dev, host, "0/1 local model");
+      }
+    } else {
+      check(ob_adam_get_state(h, OB_M_LOCAL, 0, 0, d, dev) == OB_ERR_PHASE,
+            "local momentum outside an open period");
+    }
+  }
+  compare_bits(h, o, OB_X, OBO_X, 0, d, 4, dev, host, "0/1 x");
+  compare_bits(h, o, OB_M, OBO_M, 0, d, 4, dev, host, "0/1 m");
+  compare_bits(h, o, OB_V, OBO_V, 0, d, 4, dev, host, "0/1 v");
+  compare_bits(h, o, OB_E_SERVER, OBO_E_SERVER, 0, d, 4, dev, host, "0/1 server error");
+  compare_bits(h, o, OB_SCALE_SERVER, OBO_SCALE_SERVER, 0, n, 4, dev, host, "0/1 server scales");
+  for (int w = 0; w < n; ++w) {
+    compare_bits(h, o, OB_E_WORKER, OBO_E_WORKER, w, d, 4, dev, host, "0/1 worker error");
+    compare_bits(h, o, OB_BITS_WORKER, OBO_BITS_WORKER, w, d / 64, 8, dev, host,
+                 "0/1 worker sign words");
+  }
+  int32_t bad_guard = 0;
+  OB_OK_(ob_adam_check_guards(h, &bad_guard));
+  check(bad_guard == -1, "0/1 workspace guards");
+  OB_OK_(ob_adam_destroy(h));
+  ob_oracle_destroy(o);
+  HIP_OK(hipFree(ws));
+}
+
 int main(int argc, char** argv) {
   if (argc != 3) {
     fprintf(stderr, "usage: %s d n\n", argv[0]);
@@ -124,11 +201,7 @@ int main(int argc, char** argv) {
         "compressed step before any warm-up step");
 
   for (int t = 0; t < warm + comp; ++t) {
-    for (int w = 0; w < n; ++w) {
-      for (int64_t k = 0; k < d; ++k) hg[w][k] = next_uniform(1e-2f);
-      HIP_OK(hipMemcpyAsync(dg[w], hg[w], sizeof(float) * (size_t)d, hipMemcpyHostToDevice,
-                            stream));
-    }
+    new_grads(d, n, hg, dg, stream);
     if (t < warm) {
       OB_OK_(ob_adam_warmup_step(h, (const void* const*)dg, lr));
       ob_oracle_warmup_step(o, (const void* const*)hg, 0, lr);
@@ -168,6 +241,7 @@ int main(int argc, char** argv) {
 
   OB_OK_(ob_adam_destroy(h));
   ob_oracle_destroy(o);
+  run_zero_one(d, n, hg, dg, dev, host, stream);
   for (int w = 0; w < n; ++w) {
     free(hg[w]);
     HIP_OK(hipFree(dg[w]));
@@ -179,7 +253,7 @@ int main(int argc, char** argv) {
   HIP_OK(hipFree(ws));
   HIP_OK(hipStreamDestroy(stream));
   if (failures) return 5;
-  printf("c driver ok: d=%lld n=%d, %d warm-up + %d compressed steps match the oracle\n",
-         (long long)d, n, warm, comp);
+  printf("c driver ok: d=%lld n=%d, %d warm-up + %d compressed steps and a 0/1 run match "
+         "the oracle\n", (long long)d, n, warm, comp);
   return 0;
 }

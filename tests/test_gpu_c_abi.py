@@ -2,7 +2,9 @@
 Python, no torch, device memory from hipMalloc): warm-up and compressed steps
 for the few-worker, generic and subtree-table server forms, every field read
 back through ob_adam_get_state and compared with the CPU oracle; error paths
-and the workspace guards.  The driver runs as a child process."""
+and the workspace guards; then a 0/1 Adam handle through local steps,
+synchronizations and a variance refresh, every field (the open period's local
+ones too) bit-identical to the oracle's.  The driver runs as a child process."""
 import os
 import subprocess
 
