@@ -90,6 +90,8 @@ bool grad_aligned(const ob_adam_t h, const void* g) {
   return aligned(g, h->st.grad_bf16 ? 2 : 4);
 }
 
+constexpr int32_t kDebugFlags = OB_DEBUG_SYNC | OB_DEBUG_GUARDS | OB_DEBUG_SEPARATE_SCALES;
+
 ob_status check_config(const ob_adam_config* cfg) {
   if (cfg == nullptr) return OB_ERR_ARG;
   if (cfg->grad_dtype != OB_GRAD_F32 && cfg->grad_dtype != OB_GRAD_BF16) return OB_ERR_ARG;
@@ -219,22 +221,36 @@ void bias_corrections(const ob::State& s, int64_t t, float* bc1, float* bc2) {
   *bc2 = (float)(1.0 - p2);
 }
 
-// Worker scales, server pass, server scales, update on state `s` (the
-// handle's, or the handle's with its scratch elsewhere); then count the step.
-ob_status finish_step(ob_adam_t h, const ob::State& s, float lr) {
+// After the worker pass(es) of a compressed or synchronizing step: worker
+// scales, server pass, server scales, update with step size `lr` on state
+// `s` (the handle's, or the handle's with its scratch elsewhere).  Short rows
+// of partials have their scales folded inside the server pass and the
+// update (three dispatches a step) unless OB_DEBUG_SEPARATE_SCALES asks for
+// the finalize dispatches.
+hipError_t server_and_update(ob_adam_t h, const ob::State& s, float lr) {
   hipStream_t st = h->stream;
-  hipError_t e = timed(h, OB_K_WORKER_SCALE, [&](hipEvent_t a, hipEvent_t b) {
-    return ob::launch_worker_scales(s, st, a, b);
-  });
+  const bool fold = !(h->debug & OB_DEBUG_SEPARATE_SCALES) && ob::scales_in_consumers(s);
+  hipError_t e = hipSuccess;
+  if (!fold)
+    e = timed(h, OB_K_WORKER_SCALE, [&](hipEvent_t a, hipEvent_t b) {
+      return ob::launch_worker_scales(s, st, a, b);
+    });
   if (e == hipSuccess)
-    e = timed(h, OB_K_SERVER,
-              [&](hipEvent_t a, hipEvent_t b) { return ob::launch_server_pass(s, st, a, b); });
-  if (e == hipSuccess)
+    e = timed(h, OB_K_SERVER, [&](hipEvent_t a, hipEvent_t b) {
+      return ob::launch_server_pass(s, fold, st, a, b);
+    });
+  if (e == hipSuccess && !fold)
     e = timed(h, OB_K_SERVER_SCALE,
               [&](hipEvent_t a, hipEvent_t b) { return ob::launch_server_scales(s, st, a, b); });
   if (e == hipSuccess)
     e = timed(h, OB_K_UPDATE,
-              [&](hipEvent_t a, hipEvent_t b) { return ob::launch_update(s, lr, st, a, b); });
+              [&](hipEvent_t a, hipEvent_t b) { return ob::launch_update(s, lr, fold, st, a, b); });
+  return e;
+}
+
+// The rest of a compressed step after its worker pass(es); then count it.
+ob_status finish_step(ob_adam_t h, const ob::State& s, float lr) {
+  const hipError_t e = server_and_update(h, s, lr);
   if (e != hipSuccess) return fail(h, e);
   h->steps += 1;
   h->compressed += 1;
@@ -292,7 +308,7 @@ ob_adam_handle* make_handle(const ob_adam_config* cfg, void* workspace, void* st
   }
   h->stream = (hipStream_t)stream;
   const char* dbg = getenv("OB_DEBUG");
-  if (dbg != nullptr) h->debug = atoi(dbg) & (OB_DEBUG_SYNC | OB_DEBUG_GUARDS);
+  if (dbg != nullptr) h->debug = atoi(dbg) & kDebugFlags;
   return h;
 }
 
@@ -523,20 +539,8 @@ ob_status ob_adam_zero_one_step(ob_adam_t h, const void* const* grads, float lr,
     hipError_t e = timed(h, OB_K_WORKER, [&](hipEvent_t a, hipEvent_t b) {
       return ob::launch_zo_sync(s, g, first, h->zsynced, wk, stm, a, b);
     });
-    if (e == hipSuccess)
-      e = timed(h, OB_K_WORKER_SCALE, [&](hipEvent_t a, hipEvent_t b) {
-        return ob::launch_worker_scales(s, stm, a, b);
-      });
-    if (e == hipSuccess)
-      e = timed(h, OB_K_SERVER,
-                [&](hipEvent_t a, hipEvent_t b) { return ob::launch_server_pass(s, stm, a, b); });
-    if (e == hipSuccess)
-      e = timed(h, OB_K_SERVER_SCALE, [&](hipEvent_t a, hipEvent_t b) {
-        return ob::launch_server_scales(s, stm, a, b);
-      });
     if (e == hipSuccess)  // the shared model takes the whole period's steps
-      e = timed(h, OB_K_UPDATE,
-                [&](hipEvent_t a, hipEvent_t b) { return ob::launch_update(s, gamma, stm, a, b); });
+      e = server_and_update(h, s, gamma);
     if (e == hipSuccess && refresh)  // after the update, which used the stale variance
       e = timed(h, OB_K_ZO_REFRESH,
                 [&](hipEvent_t a, hipEvent_t b) { return ob::launch_zo_refresh(s, g, stm, a, b); });
@@ -652,7 +656,7 @@ ob_status ob_adam_check_guards(ob_adam_t h, int32_t* first_bad) {
 }
 
 ob_status ob_adam_set_debug(ob_adam_t h, int32_t flags) {
-  if (h == nullptr || (flags & ~(OB_DEBUG_SYNC | OB_DEBUG_GUARDS)) != 0) return OB_ERR_ARG;
+  if (h == nullptr || (flags & ~kDebugFlags) != 0) return OB_ERR_ARG;
   h->debug = flags;
   return OB_OK;
 }

@@ -81,11 +81,20 @@ hipError_t launch_warmup_finish(const State& s, float lr, float bc1, float bc2,
                                 hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw, bool m_bits,
                               hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+// Whether a step's per-chunk scales can be folded by the passes that consume
+// them -- every server block its chunk's worker rows, every update block the
+// server rows -- instead of by dispatches of their own: rows of at most 64
+// partials, and at most 1024 partials read per block.  The scales are the
+// same bits either way.  With fold_scales, launch_server_pass and
+// launch_update do it and launch_worker_scales / launch_server_scales are not
+// called.
+bool scales_in_consumers(const State& s);
 hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
-hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_server_pass(const State& s, bool fold_scales, hipStream_t stream,
+                              hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
-hipError_t launch_update(const State& s, float lr, hipStream_t stream, hipEvent_t t0,
-                         hipEvent_t t1);
+hipError_t launch_update(const State& s, float lr, bool fold_scales, hipStream_t stream,
+                         hipEvent_t t0, hipEvent_t t1);
 // 0/1 Adam: a local step of all workers (first: the first step of a local
 // period; m_bits: the shared momentum is held as server sign words), the
 // synchronizing step's worker pass (then worker scales, server pass, server

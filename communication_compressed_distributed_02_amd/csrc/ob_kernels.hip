@@ -40,7 +40,13 @@
 //    server pass for 32 and 64 workers writes one per segment.
 //  - Per-chunk scales come from small kernels: one dispatch that folds a
 //    chunk's partials in registers and one block, or aligned groups of 512
-//    partials folded in parallel and then one block per chunk.
+//    partials folded in parallel and then one block per chunk.  Where the
+//    rows of partials are short (at most 64, as on 1M-parameter shapes),
+//    the passes that need the scales fold them themselves -- every server
+//    block its chunk's worker rows, every update block the server rows -- in
+//    the same order, and a step is three dispatches.
+#include <algorithm>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -643,6 +649,47 @@ __global__ void __launch_bounds__(kBlock)
   }
 }
 
+// Scale of one chunk from a row of `count` <= 64 partials, by one wave:
+// lane t takes partial t (+0 past the row, as the finalize kernels pad), and
+// an xor butterfly over offsets 1, 2, ..., 32 adds sibling subtrees level by
+// level.  IEEE addition commutes, so every lane ends with the row's
+// pairwise-by-levels sum, the value the finalize kernels fold, and the scale
+// is formed as they form it.
+__device__ __forceinline__ float row_scale_wave(const double* __restrict__ p, int64_t count,
+                                                int64_t L, int lane) {
+  double v = lane < count ? p[lane] : 0.0;
+#pragma unroll
+  for (int o = 1; o <= 32; o <<= 1) v = v + __shfl_xor(v, o, 64);
+  return (float)(sqrt(v) / sqrt((double)L));
+}
+
+// Scales of `rows` chunks folded inside a consuming pass: row r's `count`
+// <= 64 partials start at part + r*pstride, one wave per row.  They go to
+// lds[r] (visible to the whole block after the barrier) and, when `store`
+// (one block per set of rows), to out[r*ostride], where the next step's
+// passes and the state readback find them.  Every thread of the block must
+// reach it.
+__device__ __forceinline__ void fold_scales_in_block(const double* __restrict__ part,
+                                                     int64_t pstride, int64_t count, int rows,
+                                                     int64_t L, float* lds,
+                                                     float* __restrict__ out, int64_t ostride,
+                                                     bool store) {
+  const int lane = threadIdx.x & 63;
+  for (int r = wave_in_block(); r < rows; r += kWavesPerBlock) {
+    const float sc = row_scale_wave(part + r * pstride, count, L, lane);
+    if (lane == 0) {
+      lds[r] = sc;
+      if (store) out[r * ostride] = sc;
+    }
+  }
+  __syncthreads();
+}
+
+// A uniform copy of an LDS value (kept in a scalar register).
+__device__ __forceinline__ float uniform_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 // ------------------------------------------------------------- server pass --
 // Server j: a = pairwise over workers of (bit ? s_wj : -s_wj) / n;
 // u = a + (u_prev - (u_prev >= 0 ? s_prev : -s_prev)); stores u, sign words,
@@ -697,12 +744,17 @@ __device__ __forceinline__ void server_average_segment(const uint64_t* __restric
   for (int r = 0; r < kSegRows; ++r) avg[r] = stack[LEVELS - 1][r] / (float)NW;
 }
 
-// NW = 1, 2, 4, or 0 for a run-time worker count.
-template <int NW>
+// NW = 1, 2, 4, or 0 for a run-time worker count.  FOLD: the worker scales
+// of chunk j are folded here from the worker pass's partials (`wcount` per
+// row), and the chunk's first block stores them to wscale_out; otherwise
+// they are read from wscale (the two pointers name the same buffer; a launch
+// uses one of them).
+template <int NW, bool FOLD>
 __global__ void __launch_bounds__(kBlock)
     server_kernel(int64_t L, int n, int64_t nseg, int64_t words,
                   const uint64_t* __restrict__ wbits, const float* __restrict__ wscale,
-                  float* __restrict__ u, const float* __restrict__ sscale_prev,
+                  float* __restrict__ wscale_out, const double* __restrict__ wpart,
+                  int64_t wcount, float* __restrict__ u, const float* __restrict__ sscale_prev,
                   uint64_t* __restrict__ sbits, double* __restrict__ spart) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.y;
@@ -710,14 +762,17 @@ __global__ void __launch_bounds__(kBlock)
   // in LDS for a run-time one
   constexpr int WS = NW > 0 ? NW : 1;
   float ws[WS];
-  if constexpr (NW > 0) {
-#pragma unroll
-    for (int w = 0; w < NW; ++w) ws[w] = wscale[w * n + j];
-  }
-  __shared__ float sws[NW > 0 ? 1 : kMaxWorkersPerLaunch];
-  if constexpr (NW == 0) {
+  __shared__ float sws[NW > 0 && !FOLD ? 1 : kMaxWorkersPerLaunch];
+  if constexpr (FOLD) {
+    fold_scales_in_block(wpart + (int64_t)j * wcount, (int64_t)n * wcount, wcount, n, L, sws,
+                         wscale_out + j, n, blockIdx.x == 0);
+  } else if constexpr (NW == 0) {
     if ((int)threadIdx.x < n) sws[threadIdx.x] = wscale[threadIdx.x * n + j];
     __syncthreads();
+  }
+  if constexpr (NW > 0) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) ws[w] = FOLD ? uniform_f32(sws[w]) : wscale[w * n + j];
   }
   const float sp = sscale_prev[j];
   __shared__ double quad_part[kWavesPerBlock];
@@ -877,21 +932,28 @@ __device__ __forceinline__ void server_average_groups(const uint64_t* __restrict
 // went 6 % slower) or a wave-contiguous order (19 % more sign-word fetches).
 // Otherwise the block's 4 waves take one segment each of a quad and fold
 // their partials in LDS.
-template <int NG, bool SEG_PARTIALS>
+// FOLD as in server_kernel.
+template <int NG, bool SEG_PARTIALS, bool FOLD>
 __global__ void __launch_bounds__(kBlock)
     server_groups_kernel(int64_t L, int n, int64_t nseg, int64_t words,
                          const uint64_t* __restrict__ wbits, const float* __restrict__ wscale,
-                         float* __restrict__ u, const float* __restrict__ sscale_prev,
-                         uint64_t* __restrict__ sbits, double* __restrict__ spart) {
+                         float* __restrict__ wscale_out, const double* __restrict__ wpart,
+                         int64_t wcount, float* __restrict__ u,
+                         const float* __restrict__ sscale_prev, uint64_t* __restrict__ sbits,
+                         double* __restrict__ spart) {
   __shared__ float tab[NG * 256];
+  __shared__ float sws[FOLD ? 8 * NG : 1];
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.y;
+  if constexpr (FOLD)
+    fold_scales_in_block(wpart + (int64_t)j * wcount, (int64_t)n * wcount, wcount, 8 * NG, L, sws,
+                         wscale_out + j, n, blockIdx.x == 0);
   for (int t = threadIdx.x; t < NG * 256; t += kBlock) {
     const int g = t >> 8, i = t & 255;
     float v[8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const float sc = wscale[(8 * g + b) * n + j];
+      const float sc = FOLD ? sws[8 * g + b] : wscale[(8 * g + b) * n + j];
       v[b] = ((i >> b) & 1) ? sc : -sc;
     }
     tab[t] = pairwise_sum<8>(v);
@@ -969,11 +1031,23 @@ __device__ __forceinline__ float update_one(float x, float v, float mv, float lr
   return x - lr * (mv / (sqrtf(v) + eps));
 }
 
+// FOLD: the n server scales are folded by every block from the server pass's
+// partials (`scount` per row) and the grid's first block stores them to
+// sscale_out; otherwise they are read from sscale (the same buffer).
+template <bool FOLD>
 __global__ void __launch_bounds__(kBlock)
-    update_kernel(int64_t words, int64_t L, const uint64_t* __restrict__ sbits,
-                  const float* __restrict__ sscale, const float* __restrict__ v,
+    update_kernel(int64_t words, int64_t L, int n, const uint64_t* __restrict__ sbits,
+                  const float* __restrict__ sscale, float* __restrict__ sscale_out,
+                  const double* __restrict__ spart, int64_t scount, const float* __restrict__ v,
                   float* __restrict__ x, float lr, float eps) {
   const int lane = threadIdx.x & 63;
+  __shared__ float fss[FOLD ? kMaxWorkersPerLaunch : 1];
+  if constexpr (FOLD)
+    fold_scales_in_block(spart, scount, scount, n, L, fss, sscale_out, 1, blockIdx.x == 0);
+  auto scale_of = [&](int64_t jj) -> float {
+    if constexpr (FOLD) return fss[jj];
+    return sscale[jj];
+  };
   const int64_t ngroups = (words + kSegRows - 1) / kSegRows;
   const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t rows_per_chunk = L >> 6;
@@ -985,7 +1059,7 @@ __global__ void __launch_bounds__(kBlock)
     // the 16 rows lie in one chunk unless a chunk boundary falls inside them
     const bool one_chunk = rows == kSegRows && (r0 + kSegRows - 1) / rows_per_chunk == j0;
     if (one_chunk) {
-      const float s = sscale[j0];
+      const float s = scale_of(j0);
       float xv[kSegRows], vv[kSegRows];
 #pragma unroll
       for (int r = 0; r < kSegRows; ++r) {
@@ -999,7 +1073,7 @@ __global__ void __launch_bounds__(kBlock)
     } else {
       for (int r = 0; r < rows; ++r) {
         const int64_t row = r0 + r;
-        const float s = sscale[row / rows_per_chunk];
+        const float s = scale_of(row / rows_per_chunk);
         const int64_t k = row * 64 + lane;
         x[k] = update_one(x[k], v[k], signed_scale(sbits[row], s), lr, eps);
       }
@@ -1292,21 +1366,41 @@ static hipError_t launch_scales(const double* part, int64_t nseg, int64_t L, int
                 (const double*)fold, ngroups, L, scale_out);
 }
 
-hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  // the worker pass leaves one partial per block of 4 segments
-  return launch_scales(s.wpart, quads(s.nseg), s.L, s.n * s.n, s.fold, s.wscale, stream, t0, t1);
+// Partials per row left by the worker pass (one per block of 4 segments) and
+// by the server pass (the same, or one per segment with 32 and 64 workers).
+static int64_t worker_row_partials(const State& s) { return quads(s.nseg); }
+static int64_t server_row_partials(const State& s) {
+  return server_segment_partials(s.n) ? s.nseg : quads(s.nseg);
 }
 
-hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+bool scales_in_consumers(const State& s) {
+  const int64_t longest = std::max(worker_row_partials(s), server_row_partials(s));
+  return longest <= 64 && (int64_t)s.n * longest <= 1024;
+}
+
+hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  return launch_scales(s.wpart, worker_row_partials(s), s.L, s.n * s.n, s.fold, s.wscale, stream,
+                       t0, t1);
+}
+
+hipError_t launch_server_pass(const State& s, bool fold_scales, hipStream_t stream,
+                              hipEvent_t t0, hipEvent_t t1) {
+  const int64_t wcount = worker_row_partials(s);
   if (s.n == 8 || s.n == 16 || s.n == 32 || s.n == 64) {
     // segments per wave (measured): 1 up to 16 workers, 4 beyond (the tables
     // are built once per block)
     const int per_wave = s.n <= 16 ? 1 : 4;
     const dim3 grid(grid_for(s.nseg, kWavesPerBlock * per_wave, kMaxBlocksPerRow), (unsigned)s.n);
-#define OB_SRVG(NG, WQ)                                                                        \
-  return launch(server_groups_kernel<NG, WQ>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n,     \
-                s.nseg, s.words, (const uint64_t*)s.wbits, (const float*)s.wscale, s.u,         \
-                (const float*)s.sscale, s.sbits, s.spart)
+#define OB_SRVG(NG, WQ)                                                                          \
+  return fold_scales                                                                             \
+             ? launch(server_groups_kernel<NG, WQ, true>, grid, dim3(kBlock), stream, t0, t1, s.L, \
+                      s.n, s.nseg, s.words, (const uint64_t*)s.wbits, (const float*)s.wscale,    \
+                      s.wscale, (const double*)s.wpart, wcount, s.u, (const float*)s.sscale,     \
+                      s.sbits, s.spart)                                                          \
+             : launch(server_groups_kernel<NG, WQ, false>, grid, dim3(kBlock), stream, t0, t1,    \
+                      s.L, s.n, s.nseg, s.words, (const uint64_t*)s.wbits,                       \
+                      (const float*)s.wscale, s.wscale, (const double*)s.wpart, wcount, s.u,     \
+                      (const float*)s.sscale, s.sbits, s.spart)
     switch (s.n) {
       case 8: OB_SRVG(1, false);
       case 16: OB_SRVG(2, false);
@@ -1316,10 +1410,16 @@ hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0,
 #undef OB_SRVG
   }
   const dim3 grid(grid_for(s.nseg, kWavesPerBlock, kMaxBlocksPerRow), (unsigned)s.n);
-#define OB_SRV(NW)                                                                             \
-  return launch(server_kernel<NW>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n, s.nseg,       \
-                s.words, (const uint64_t*)s.wbits, (const float*)s.wscale, s.u,                 \
-                (const float*)s.sscale, s.sbits, s.spart)
+#define OB_SRV(NW)                                                                               \
+  return fold_scales                                                                             \
+             ? launch(server_kernel<NW, true>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n,      \
+                      s.nseg, s.words, (const uint64_t*)s.wbits, (const float*)s.wscale,         \
+                      s.wscale, (const double*)s.wpart, wcount, s.u, (const float*)s.sscale,     \
+                      s.sbits, s.spart)                                                          \
+             : launch(server_kernel<NW, false>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n,     \
+                      s.nseg, s.words, (const uint64_t*)s.wbits, (const float*)s.wscale,         \
+                      s.wscale, (const double*)s.wpart, wcount, s.u, (const float*)s.sscale,     \
+                      s.sbits, s.spart)
   switch (s.n) {
     case 1: OB_SRV(1);
     case 2: OB_SRV(2);
@@ -1330,18 +1430,18 @@ hipError_t launch_server_pass(const State& s, hipStream_t stream, hipEvent_t t0,
 }
 
 hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  // the server passes leave one partial per block of 4 segments, or per
-  // segment with 32 and 64 workers
-  const int64_t count = server_segment_partials(s.n) ? s.nseg : quads(s.nseg);
-  return launch_scales(s.spart, count, s.L, s.n, s.fold, s.sscale, stream, t0, t1);
+  return launch_scales(s.spart, server_row_partials(s), s.L, s.n, s.fold, s.sscale, stream, t0,
+                       t1);
 }
 
-hipError_t launch_update(const State& s, float lr, hipStream_t stream, hipEvent_t t0,
-                         hipEvent_t t1) {
+hipError_t launch_update(const State& s, float lr, bool fold_scales, hipStream_t stream,
+                         hipEvent_t t0, hipEvent_t t1) {
   const int64_t groups = (s.words + kSegRows - 1) / kSegRows;
-  return launch(update_kernel, dim3(grid_for(groups, kWavesPerBlock, kMaxBlocksPerRow)),
-                dim3(kBlock), stream, t0, t1, s.words, s.L, (const uint64_t*)s.sbits,
-                (const float*)s.sscale, (const float*)s.v, s.x, lr, s.eps);
+  const dim3 grid(grid_for(groups, kWavesPerBlock, kMaxBlocksPerRow));
+  return launch(fold_scales ? update_kernel<true> : update_kernel<false>, grid, dim3(kBlock),
+                stream, t0, t1, s.words, s.L, s.n, (const uint64_t*)s.sbits,
+                (const float*)s.sscale, s.sscale, (const double*)s.spart, server_row_partials(s),
+                (const float*)s.v, s.x, lr, s.eps);
 }
 
 hipError_t launch_error_out(const float* comp, const float* scales, int64_t L, int64_t offset,

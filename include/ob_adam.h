@@ -305,10 +305,18 @@ ob_status ob_adam_check_guards(ob_adam_t h, int32_t* first_bad);
  *                    with its OB_K_* id) by the call that launched it;
  *  OB_DEBUG_GUARDS - after every completed step the workspace guards are
  *                    checked; a changed guard is reported on stderr, the
- *                    handle is poisoned and the step returns OB_ERR_HIP.
- * Both make every call synchronous; the results are unchanged.  OB_ERR_ARG
- * for other flag bits. */
-enum { OB_DEBUG_SYNC = 1, OB_DEBUG_GUARDS = 2 };
+ *                    handle is poisoned and the step returns OB_ERR_HIP;
+ *  OB_DEBUG_SEPARATE_SCALES - the per-chunk scales always come from
+ *                    finalize dispatches of their own.  Without it, shapes
+ *                    whose chunks leave at most 64 partials per row (and n
+ *                    times that at most 1024; chunks of up to 256K elements
+ *                    for n <= 16) have them folded inside the server pass
+ *                    and the update, in the same order: a step is then three
+ *                    dispatches, and OB_K_WORKER_SCALE / OB_K_SERVER_SCALE
+ *                    record no launches.
+ * The first two make every call synchronous.  None changes a result bit.
+ * OB_ERR_ARG for other flag bits. */
+enum { OB_DEBUG_SYNC = 1, OB_DEBUG_GUARDS = 2, OB_DEBUG_SEPARATE_SCALES = 4 };
 ob_status ob_adam_set_debug(ob_adam_t h, int32_t flags);
 
 /* Steps taken so far (warm-up and compressed) and compressed steps taken. */
