@@ -122,6 +122,8 @@ def ob_adam_init(cfg, workspace_ptr, ws_bytes, x0_ptr, stream_ptr):
 
 
 def _ptr_array(ptrs):
+    if isinstance(ptrs, ctypes.Array):  # marshalled already (GradBatch)
+        return ptrs
     return (ctypes.c_void_p * len(ptrs))(*ptrs)
 
 
@@ -186,7 +188,7 @@ def ob_adam_check_guards(h):
     return bad.value
 
 
-OB_DEBUG_SYNC, OB_DEBUG_GUARDS = 1, 2
+OB_DEBUG_SYNC, OB_DEBUG_GUARDS, OB_DEBUG_SEPARATE_SCALES = 1, 2, 4
 
 
 def ob_adam_set_debug(h, flags):
@@ -229,6 +231,27 @@ _FIELD_DTYPE = {OB_X: torch.float32, OB_M: torch.float32, OB_V: torch.float32,
                 OB_BITS_WORKER: torch.int64, OB_BITS_SERVER: torch.int64,
                 OB_SCALE_WORKER: torch.float32, OB_SCALE_SERVER: torch.float32,
                 OB_M_LOCAL: torch.float32, OB_A_LOCAL: torch.float32, OB_X_LOCAL: torch.float32}
+
+
+class GradBatch:
+    """The n gradients of one step, checked and marshalled once
+    (OneBitAdam.bind_grads); the step calls take it in place of the list and
+    skip the per-call checks.  It holds the tensors, whose contents may change
+    between steps; indexing gives worker i's tensor."""
+    __slots__ = ("tensors", "ptrs")
+
+    def __init__(self, tensors, ptrs):
+        self.tensors = tuple(tensors)
+        self.ptrs = _ptr_array(ptrs)
+
+    def __len__(self):
+        return len(self.tensors)
+
+    def __getitem__(self, i):
+        return self.tensors[i]
+
+    def __iter__(self):
+        return iter(self.tensors)
 
 
 class OneBitAdam:
@@ -281,11 +304,27 @@ class OneBitAdam:
             for t in tensors:
                 t.record_stream(self.stream)
 
-    def _order_caller_after(self):
-        if self._separate():
-            torch.cuda.current_stream(self.device).wait_stream(self.stream)
+    def _ordered(self, tensors, fn, *args):
+        """fn(*args) on the library's stream, ordered after the caller's
+        current stream and the caller's stream after it (tensors recorded on
+        the library's stream when the two differ); one stream query."""
+        cur = torch.cuda.current_stream(self.device)
+        if cur == self.stream:
+            fn(*args)
+            return
+        self.stream.wait_stream(cur)
+        for t in tensors:
+            t.record_stream(self.stream)
+        fn(*args)
+        cur.wait_stream(self.stream)
 
-    def _grad_ptrs(self, grads):
+    def _grad_ptrs(self, grads, count=None):
+        """Device pointers of `count` (default n) checked gradient tensors."""
+        count = self.n if count is None else count
+        if len(grads) != count:
+            raise ValueError("%d gradients given, %d expected" % (len(grads), count))
+        if isinstance(grads, GradBatch):
+            return grads.ptrs
         want = torch.bfloat16 if self.cfg.grad_dtype == OB_GRAD_BF16 else torch.float32
         ptrs = []
         for g in grads:
@@ -294,56 +333,40 @@ class OneBitAdam:
             ptrs.append(g.data_ptr())
         return ptrs
 
+    def bind_grads(self, grads):
+        """A GradBatch of one step's n gradient tensors (checked here once)."""
+        return GradBatch(grads, self._grad_ptrs(grads))
+
     def warmup_step(self, grads, lr):
-        ptrs = self._grad_ptrs(grads)
-        self._order_after_caller(*grads)
-        ob_adam_warmup_step(self.h, ptrs, lr)
-        self._order_caller_after()
+        self._ordered(grads, ob_adam_warmup_step, self.h, self._grad_ptrs(grads), lr)
 
     def warmup_worker(self, worker, grad):
-        ptr = self._grad_ptrs([grad])[0]
-        self._order_after_caller(grad)
-        ob_adam_warmup_worker(self.h, worker, ptr)
-        self._order_caller_after()
+        self._ordered((grad,), ob_adam_warmup_worker, self.h, worker,
+                      self._grad_ptrs([grad], 1)[0])
 
     def warmup_finish(self, lr):
-        self._order_after_caller()
-        ob_adam_warmup_finish(self.h, lr)
-        self._order_caller_after()
+        self._ordered((), ob_adam_warmup_finish, self.h, lr)
 
     def compressed_step(self, grads, lr):
-        ptrs = self._grad_ptrs(grads)
-        self._order_after_caller(*grads)
-        ob_adam_compressed_step(self.h, ptrs, lr)
-        self._order_caller_after()
+        self._ordered(grads, ob_adam_compressed_step, self.h, self._grad_ptrs(grads), lr)
 
     def compressed_step_static(self, grads, lr):
         """compressed_step with the step's scratch in the library's static
         array (allocates nothing)."""
-        ptrs = self._grad_ptrs(grads)
-        self._order_after_caller(*grads)
-        ob_adam_compressed_step_static(self.h, ptrs, lr)
-        self._order_caller_after()
+        self._ordered(grads, ob_adam_compressed_step_static, self.h, self._grad_ptrs(grads), lr)
 
     def zero_one_step(self, grads, lr, sync, refresh=False):
         """One 0/1 Adam step; `sync` closes the local period, `refresh` (only
         with sync) refreshes the stale variance."""
-        ptrs = self._grad_ptrs(grads)
-        self._order_after_caller(*grads)
-        ob_adam_zero_one_step(self.h, ptrs, lr,
-                              (OB_ZO_SYNC if sync else 0) | (OB_ZO_REFRESH if refresh else 0))
-        self._order_caller_after()
+        self._ordered(grads, ob_adam_zero_one_step, self.h, self._grad_ptrs(grads), lr,
+                      (OB_ZO_SYNC if sync else 0) | (OB_ZO_REFRESH if refresh else 0))
 
     def compress_worker(self, worker, grad):
-        ptr = self._grad_ptrs([grad])[0]
-        self._order_after_caller(grad)
-        ob_adam_compress_worker(self.h, worker, ptr)
-        self._order_caller_after()
+        self._ordered((grad,), ob_adam_compress_worker, self.h, worker,
+                      self._grad_ptrs([grad], 1)[0])
 
     def compressed_finish(self, lr):
-        self._order_after_caller()
-        ob_adam_compressed_finish(self.h, lr)
-        self._order_caller_after()
+        self._ordered((), ob_adam_compressed_finish, self.h, lr)
 
     def get(self, field, worker=0, offset=0, count=None):
         """Device tensor with `count` elements of a field (see include/ob_adam.h)."""
@@ -352,17 +375,15 @@ class OneBitAdam:
         if count is None:
             count = size - offset
         out = torch.empty(max(count, 0), dtype=_FIELD_DTYPE[field], device=self.device)
-        self._order_after_caller(out)
-        ob_adam_get_state(self.h, field, worker, offset, count, out.data_ptr() if count else None)
-        self._order_caller_after()
+        self._ordered((out,), ob_adam_get_state, self.h, field, worker, offset, count,
+                      out.data_ptr() if count else None)
         return out
 
     def set(self, field, src, offset=0):
         if src.dtype != torch.float32 or not src.is_contiguous():
             raise ValueError("source must be a contiguous float32 tensor")
-        self._order_after_caller(src)
-        ob_adam_set_state(self.h, field, offset, src.numel(), src.data_ptr())
-        self._order_caller_after()
+        self._ordered((src,), ob_adam_set_state, self.h, field, offset, src.numel(),
+                      src.data_ptr())
 
     def checkpoint(self, device="cpu"):
         """(copy of the workspace bytes, counters): the whole optimizer state."""

@@ -493,3 +493,39 @@ def test_debug_mode_same_results_and_reports_a_changed_guard():
     with pytest.raises(ob.ObAdamError) as e:  # poisoned
         other.compressed_step(g, 1e-3)
     assert e.value.status == ob.OB_ERR_HIP
+
+
+def test_bound_gradient_batches_equal_lists():
+    """Gradients bound once (OneBitAdam.bind_grads) give the same bits as the
+    same tensors passed as lists, for warm-up, compressed and staged calls;
+    a batch or list of the wrong length is refused before any launch."""
+    import torch
+    d, n = 4 * 3392, 4
+    a = ob.OneBitAdam(d, n)
+    b = ob.OneBitAdam(d, n)
+    lists = [[to_device_grad(g) for g in host_grads(d, n, t)] for t in range(5)]
+    bound = [b.bind_grads(g) for g in lists]
+    for t in range(5):
+        lr = np.float32(1e-3 * (1 + t))
+        if t < 2:
+            a.warmup_step(lists[t], lr)
+            b.warmup_step(bound[t], lr)
+        elif t < 4:
+            a.compressed_step(lists[t], lr)
+            b.compressed_step(bound[t], lr)
+        else:
+            for i in range(n):
+                a.compress_worker(i, lists[t][i])
+                b.compress_worker(i, bound[t][i])
+            a.compressed_finish(lr)
+            b.compressed_finish(lr)
+    torch.cuda.synchronize()
+    for f, w in [(ob.OB_X, 0), (ob.OB_M, 0), (ob.OB_E_SERVER, 0)] + \
+            [(ob.OB_E_WORKER, w) for w in range(n)]:
+        assert torch.equal(a.get(f, w), b.get(f, w)), (f, w)
+    with pytest.raises(ValueError):
+        a.compressed_step(lists[0][:3], 1e-3)
+    with pytest.raises(ValueError):
+        ob.OneBitAdam(d, 2).compressed_step(bound[0], 1e-3)
+    with pytest.raises(ValueError):
+        a.bind_grads(lists[0] + lists[1][:1])
