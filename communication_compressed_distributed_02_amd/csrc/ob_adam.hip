@@ -90,7 +90,16 @@ bool grad_aligned(const ob_adam_t h, const void* g) {
   return aligned(g, h->st.grad_bf16 ? 2 : 4);
 }
 
-constexpr int32_t kDebugFlags = OB_DEBUG_SYNC | OB_DEBUG_GUARDS | OB_DEBUG_SEPARATE_SCALES;
+constexpr int32_t kDebugFlags = OB_DEBUG_SYNC | OB_DEBUG_GUARDS | OB_DEBUG_SEPARATE_SCALES |
+                                OB_DEBUG_UNSTAGED_SERVER | OB_DEBUG_SMALL_LAUNCHES;
+// elements per launch of a streaming pass under OB_DEBUG_SMALL_LAUNCHES: one
+// block of 4 segments, so small shapes take many launches per pass
+constexpr int64_t kSmallLaunchElems = 4 * ob::kSegElems;
+
+void set_debug_flags(ob_adam_handle* h, int32_t flags) {
+  h->debug = flags;
+  h->st.launch_elems = (flags & OB_DEBUG_SMALL_LAUNCHES) ? kSmallLaunchElems : 0;
+}
 
 ob_status check_config(const ob_adam_config* cfg) {
   if (cfg == nullptr) return OB_ERR_ARG;
@@ -226,7 +235,8 @@ void bias_corrections(const ob::State& s, int64_t t, float* bc1, float* bc2) {
 // `s` (the handle's, or the handle's with its scratch elsewhere).  Short rows
 // of partials have their scales folded inside the server pass and the
 // update (three dispatches a step) unless OB_DEBUG_SEPARATE_SCALES asks for
-// the finalize dispatches.
+// the finalize dispatches; OB_DEBUG_UNSTAGED_SERVER keeps the server pass's
+// sign words out of LDS.
 hipError_t server_and_update(ob_adam_t h, const ob::State& s, float lr) {
   hipStream_t st = h->stream;
   const bool fold = !(h->debug & OB_DEBUG_SEPARATE_SCALES) && ob::scales_in_consumers(s);
@@ -237,7 +247,7 @@ hipError_t server_and_update(ob_adam_t h, const ob::State& s, float lr) {
     });
   if (e == hipSuccess)
     e = timed(h, OB_K_SERVER, [&](hipEvent_t a, hipEvent_t b) {
-      return ob::launch_server_pass(s, fold, st, a, b);
+      return ob::launch_server_pass(s, fold, !(h->debug & OB_DEBUG_UNSTAGED_SERVER), st, a, b);
     });
   if (e == hipSuccess && !fold)
     e = timed(h, OB_K_SERVER_SCALE,
@@ -308,7 +318,7 @@ ob_adam_handle* make_handle(const ob_adam_config* cfg, void* workspace, void* st
   }
   h->stream = (hipStream_t)stream;
   const char* dbg = getenv("OB_DEBUG");
-  if (dbg != nullptr) h->debug = atoi(dbg) & kDebugFlags;
+  if (dbg != nullptr) set_debug_flags(h, atoi(dbg) & kDebugFlags);
   return h;
 }
 
@@ -657,7 +667,7 @@ ob_status ob_adam_check_guards(ob_adam_t h, int32_t* first_bad) {
 
 ob_status ob_adam_set_debug(ob_adam_t h, int32_t flags) {
   if (h == nullptr || (flags & ~kDebugFlags) != 0) return OB_ERR_ARG;
-  h->debug = flags;
+  set_debug_flags(h, flags);
   return OB_OK;
 }
 

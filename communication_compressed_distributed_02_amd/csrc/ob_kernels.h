@@ -24,6 +24,7 @@ struct GradPtrs {
 struct State {
   int64_t d, L, nseg, words;  // words = d/64
   int n;
+  int64_t launch_elems;  // elements per launch of a streaming pass (0: the default)
   int grad_bf16;
   float beta1, beta2, eps;
   float* x;
@@ -90,8 +91,11 @@ hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw,
 // called.
 bool scales_in_consumers(const State& s);
 hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
-hipError_t launch_server_pass(const State& s, bool fold_scales, hipStream_t stream,
-                              hipEvent_t t0, hipEvent_t t1);
+// stage_words: the 8-64-worker form stages each segment's sign words in LDS
+// (chunks of an even number of rows; others, or false, load them directly).
+// The same bits either way.
+hipError_t launch_server_pass(const State& s, bool fold_scales, bool stage_words,
+                              hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_update(const State& s, float lr, bool fold_scales, hipStream_t stream,
                          hipEvent_t t0, hipEvent_t t1);

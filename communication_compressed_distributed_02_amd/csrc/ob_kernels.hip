@@ -67,6 +67,15 @@ __host__ __device__ constexpr int64_t quads(int64_t nseg) {
   return (nseg + kWavesPerBlock - 1) / kWavesPerBlock;
 }
 
+// The part of a pass's grid that one launch covers: block (x, y) of the
+// launch is block (bx0 + x, by0 + y) of the whole pass.  The update, whose
+// waves stride over groups of 16 rows, takes the groups [lo, hi) instead.
+struct Part {
+  int64_t bx0;
+  int by0;
+  int64_t lo, hi;
+};
+
 // The server pass for 32 and 64 workers leaves one partial per segment; every
 // other pass leaves one per block of 4 segments.
 constexpr bool server_segment_partials(int n) { return n == 32 || n == 64; }
@@ -332,7 +341,7 @@ __device__ __forceinline__ void worker_row(const GT* __restrict__ g, float* __re
 // twice, held 42-50 VGPRs against 32-37 without it.
 template <typename GT, bool MBITS>
 __global__ void __launch_bounds__(kBlock)
-    worker_kernel(GradPtrs g, int w0, int64_t d, int64_t L, int n, int64_t nseg, int64_t words,
+    worker_kernel(GradPtrs g, int w0, Part pt, int64_t d, int64_t L, int n, int64_t nseg, int64_t words,
                   const float* __restrict__ m, const uint64_t* __restrict__ sbits,
                   const float* __restrict__ sscale, float* __restrict__ cbuf,
                   const float* __restrict__ wscale, uint64_t* __restrict__ wbits,
@@ -340,8 +349,9 @@ __global__ void __launch_bounds__(kBlock)
   __shared__ double quad_part[kWavesPerBlock];
   const int lane = threadIdx.x & 63;
   const int wv = wave_in_block();
-  const int wi = (int)blockIdx.y / n;  // worker within this launch
-  const int j = (int)blockIdx.y - wi * n;
+  const int y = pt.by0 + (int)blockIdx.y;
+  const int wi = y / n;  // worker within this pass
+  const int j = y - wi * n;
   const int w = w0 + wi;
   const GT* __restrict__ gp = (const GT*)g.p[wi];
   float* __restrict__ c = cbuf + (int64_t)w * d;
@@ -351,7 +361,7 @@ __global__ void __launch_bounds__(kBlock)
   const float sp = wscale[w * n + j];  // this worker's scale of chunk j, previous step
   const float ms = MBITS ? sscale[j] : 0.0f;
   {
-    const int64_t qd = blockIdx.x;  // one quad per block (grid.x == nquad)
+    const int64_t qd = pt.bx0 + blockIdx.x;  // one quad per block
     const int64_t s = qd * kWavesPerBlock + wv;
     double acc = 0.0;
     if (s < nseg) {
@@ -420,18 +430,19 @@ __device__ __forceinline__ void zo_momentum(const GT* __restrict__ g, const floa
 // A local step (no synchronization): stores m_i and a_i.
 template <typename GT, bool FIRST, bool MBITS>
 __global__ void __launch_bounds__(kBlock)
-    zo_local_kernel(GradPtrs g, int64_t d, int64_t L, int n, int64_t nseg,
+    zo_local_kernel(GradPtrs g, Part pt, int64_t d, int64_t L, int n, int64_t nseg,
                     const float* __restrict__ m, const uint64_t* __restrict__ sbits,
                     const float* __restrict__ sscale, float* __restrict__ mlocbuf,
                     float* __restrict__ alocbuf, float beta1, float ob1, float wk) {
   const int lane = threadIdx.x & 63;
-  const int wi = (int)blockIdx.y / n;
-  const int j = (int)blockIdx.y - wi * n;
+  const int y = pt.by0 + (int)blockIdx.y;
+  const int wi = y / n;
+  const int j = y - wi * n;
   const GT* __restrict__ gp = (const GT*)g.p[wi];
   float* __restrict__ mloc = mlocbuf + (int64_t)wi * d;
   float* __restrict__ aloc = alocbuf + (int64_t)wi * d;
   const float ms = MBITS ? sscale[j] : 0.0f;
-  const int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
+  const int64_t s = (pt.bx0 + (int64_t)blockIdx.x) * kWavesPerBlock + wave_in_block();
   if (s >= nseg) return;
   const int64_t q0 = s * kSegElems;
   const int64_t left = (L - q0) >> 6;
@@ -466,7 +477,7 @@ __global__ void __launch_bounds__(kBlock)
 // squares, as in worker_kernel.
 template <typename GT, bool FIRST, bool MBITS>
 __global__ void __launch_bounds__(kBlock)
-    zo_sync_kernel(GradPtrs g, int64_t d, int64_t L, int n, int64_t nseg, int64_t words,
+    zo_sync_kernel(GradPtrs g, Part pt, int64_t d, int64_t L, int n, int64_t nseg, int64_t words,
                    const float* __restrict__ m, const uint64_t* __restrict__ sbits,
                    const float* __restrict__ sscale, const float* __restrict__ mlocbuf,
                    const float* __restrict__ alocbuf, float* __restrict__ cbuf,
@@ -475,8 +486,9 @@ __global__ void __launch_bounds__(kBlock)
   __shared__ double quad_part[kWavesPerBlock];
   const int lane = threadIdx.x & 63;
   const int wv = wave_in_block();
-  const int w = (int)blockIdx.y / n;
-  const int j = (int)blockIdx.y - w * n;
+  const int y = pt.by0 + (int)blockIdx.y;
+  const int w = y / n;
+  const int j = y - w * n;
   const GT* __restrict__ gp = (const GT*)g.p[w];
   const float* __restrict__ mloc = mlocbuf + (int64_t)w * d;
   const float* __restrict__ aloc = alocbuf + (int64_t)w * d;
@@ -486,7 +498,7 @@ __global__ void __launch_bounds__(kBlock)
   double* __restrict__ part = wpart + ((int64_t)w * n + j) * nquad;
   const float sp = wscale[w * n + j];  // this worker's scale of chunk j at the last sync
   const float ms = MBITS ? sscale[j] : 0.0f;
-  const int64_t qd = blockIdx.x;  // one quad per block (grid.x == nquad)
+  const int64_t qd = pt.bx0 + blockIdx.x;  // one quad per block
   const int64_t s = qd * kWavesPerBlock + wv;
   double acc = 0.0;
   if (s < nseg) {
@@ -751,13 +763,13 @@ __device__ __forceinline__ void server_average_segment(const uint64_t* __restric
 // uses one of them).
 template <int NW, bool FOLD>
 __global__ void __launch_bounds__(kBlock)
-    server_kernel(int64_t L, int n, int64_t nseg, int64_t words,
+    server_kernel(Part pt, int64_t L, int n, int64_t nseg, int64_t words,
                   const uint64_t* __restrict__ wbits, const float* __restrict__ wscale,
                   float* __restrict__ wscale_out, const double* __restrict__ wpart,
                   int64_t wcount, float* __restrict__ u, const float* __restrict__ sscale_prev,
                   uint64_t* __restrict__ sbits, double* __restrict__ spart) {
   const int lane = threadIdx.x & 63;
-  const int j = blockIdx.y;
+  const int j = pt.by0 + (int)blockIdx.y;
   // per-chunk worker scales: in registers for a compile-time count, staged
   // in LDS for a run-time one
   constexpr int WS = NW > 0 ? NW : 1;
@@ -765,7 +777,7 @@ __global__ void __launch_bounds__(kBlock)
   __shared__ float sws[NW > 0 && !FOLD ? 1 : kMaxWorkersPerLaunch];
   if constexpr (FOLD) {
     fold_scales_in_block(wpart + (int64_t)j * wcount, (int64_t)n * wcount, wcount, n, L, sws,
-                         wscale_out + j, n, blockIdx.x == 0);
+                         wscale_out + j, n, pt.lo == 0 && pt.bx0 + blockIdx.x == 0);
   } else if constexpr (NW == 0) {
     if ((int)threadIdx.x < n) sws[threadIdx.x] = wscale[threadIdx.x * n + j];
     __syncthreads();
@@ -778,7 +790,7 @@ __global__ void __launch_bounds__(kBlock)
   __shared__ double quad_part[kWavesPerBlock];
   const int64_t nquad = quads(nseg);
   {
-    const int64_t qd = blockIdx.x;  // one quad per block (grid.x == nquad)
+    const int64_t qd = pt.bx0 + blockIdx.x;  // one quad per block
     const int64_t s = qd * kWavesPerBlock + wave_in_block();
     // one segment: its sum of squares after the butterfly
     auto segment = [&]() -> double {
@@ -926,28 +938,95 @@ __device__ __forceinline__ void server_average_groups(const uint64_t* __restrict
   }
 }
 
+// The same average from a segment's sign words staged in LDS (see
+// stage_segment_words): st holds, for workers 8k + a (k < NG, a < 8), the
+// 16 words of the segment as 8 pieces of two rows, piece P of worker 8k + a
+// at 16-byte slot 8k*8 + 8a + (P ^ a).  Lane 8r + q reads worker 8g + q's
+// word of row 8h + r, one ds_read_b64: the xor spreads a read's 64 lanes
+// evenly over the banks.
+template <int NG>
+__device__ __forceinline__ void server_average_groups_staged(const uint64_t* st, int h,
+                                                             const float* tab, int lane,
+                                                             float* avg) {
+  uint32_t lo[NG], hi[NG];
+  const int q = lane & 7, r = lane >> 3;
+  const int slot = q * 16 + 2 * ((4 * h + (r >> 1)) ^ q) + (r & 1);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const uint64_t wd = st[g * 128 + slot];
+    lo[g] = (uint32_t)wd;
+    hi[g] = (uint32_t)(wd >> 32);
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) transpose64(lo[g], hi[g], lane);
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    float o[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const uint32_t half = rr < 4 ? lo[g] : hi[g];
+      o[g] = tab[g * 256 + __builtin_amdgcn_ubfe(half, 8 * (rr & 3), 8)];
+    }
+    avg[rr] = pairwise_sum<NG>(o) / (float)(8 * NG);
+  }
+}
+
+// Copies the sign words of one segment (rows < 16 past a ragged chunk end)
+// of all 8*NG workers into the wave's LDS area `st` with the gfx950 direct
+// global-to-LDS load (16 bytes a lane, no registers): load k moves workers
+// 8k..8k+7, lane 8a + b fetching piece b ^ a (rows 2(b^a), 2(b^a)+1) of
+// worker 8k + a, so each worker's 128-byte line is read whole, once.  Pieces
+// past a ragged end fetch the segment's first piece instead (in bounds; their
+// rows are never used).  Needs 16-byte aligned words: an even number of rows
+// per chunk.  Returns once the data is in LDS.
+template <int NG>
+__device__ __forceinline__ void stage_segment_words(const uint64_t* __restrict__ wbits,
+                                                    int64_t words, int64_t wbase, int rows,
+                                                    uint64_t* st, int lane) {
+  const int a = lane >> 3, piece = (lane & 7) ^ a;
+  const int64_t off = 2 * piece < rows ? 2 * piece : 0;
+  // the wave's previous reads of st have returned before it is overwritten
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < NG; ++k)
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(wbits + (int64_t)(8 * k + a) * words +
+                                                        wbase + off),
+        (__attribute__((address_space(3))) void*)(st + k * 128), 16, 0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // SEG_PARTIALS (32 and 64 workers, 4 segments per wave): a wave takes
-// segments strided by the grid and stores one partial per segment.  Folding
+// segments of the launch's range [pt.lo, pt.hi) strided by the launch's grid
+// and stores one partial per segment.  Folding
 // a quad's partials per block there needs a barrier per quad (the n = 64 pass
 // went 6 % slower) or a wave-contiguous order (19 % more sign-word fetches).
 // Otherwise the block's 4 waves take one segment each of a quad and fold
 // their partials in LDS.
-// FOLD as in server_kernel.
-template <int NG, bool SEG_PARTIALS, bool FOLD>
+// FOLD as in server_kernel.  STAGE (chunks of an even number of rows): the
+// sign words of each segment are staged in LDS whole (stage_segment_words)
+// instead of being loaded half a line at a time.
+template <int NG, bool SEG_PARTIALS, bool FOLD, bool STAGE>
 __global__ void __launch_bounds__(kBlock)
-    server_groups_kernel(int64_t L, int n, int64_t nseg, int64_t words,
+    server_groups_kernel(Part pt, int64_t L, int n, int64_t nseg, int64_t words,
                          const uint64_t* __restrict__ wbits, const float* __restrict__ wscale,
                          float* __restrict__ wscale_out, const double* __restrict__ wpart,
                          int64_t wcount, float* __restrict__ u,
                          const float* __restrict__ sscale_prev, uint64_t* __restrict__ sbits,
                          double* __restrict__ spart) {
   __shared__ float tab[NG * 256];
-  __shared__ float sws[FOLD ? 8 * NG : 1];
+  __shared__ uint64_t stage[STAGE ? kWavesPerBlock * NG * 128 : 1];
+  // the folded worker scales are read only while the tables are built, before
+  // the barrier that precedes any staging: with STAGE they share its area
+  // (4 blocks of 40 KB fit a CU's 160 KB at 64 workers; 256 bytes more do not)
+  __shared__ float sws_own[FOLD && !STAGE ? 8 * NG : 1];
+  float* const sws = STAGE ? reinterpret_cast<float*>(stage) : sws_own;
   const int lane = threadIdx.x & 63;
-  const int j = blockIdx.y;
+  const int j = pt.by0 + (int)blockIdx.y;
+  uint64_t* const st = stage + (STAGE ? wave_in_block() * NG * 128 : 0);
   if constexpr (FOLD)
     fold_scales_in_block(wpart + (int64_t)j * wcount, (int64_t)n * wcount, wcount, 8 * NG, L, sws,
-                         wscale_out + j, n, blockIdx.x == 0);
+                         wscale_out + j, n, pt.lo == 0 && pt.bx0 + blockIdx.x == 0);
   for (int t = threadIdx.x; t < NG * 256; t += kBlock) {
     const int g = t >> 8, i = t & 255;
     float v[8];
@@ -969,12 +1048,16 @@ __global__ void __launch_bounds__(kBlock)
     const int64_t wbase = base >> 6;
     double acc = 0.0;
     uint64_t mine = 0;
+    if constexpr (STAGE) stage_segment_words<NG>(wbits, words, wbase, rows, st, lane);
 #pragma unroll
     for (int h = 0; h < kSegRows / 8; ++h) {
       const int nrows = rows - 8 * h;  // rows of this half (<= 0 past a chunk's end)
       if (nrows <= 0) break;
       float avg[8];
-      server_average_groups<NG>(wbits, words, wbase + 8 * h, nrows, tab, lane, avg);
+      if constexpr (STAGE)
+        server_average_groups_staged<NG>(st, h, tab, lane, avg);
+      else
+        server_average_groups<NG>(wbits, words, wbase + 8 * h, nrows, tab, lane, avg);
       if (nrows >= 8) {
         float up[8];
 #pragma unroll
@@ -1010,7 +1093,7 @@ __global__ void __launch_bounds__(kBlock)
   };
   if constexpr (SEG_PARTIALS) {
     const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); s < nseg;
+    for (int64_t s = pt.lo + (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); s < pt.hi;
          s += nwave) {
       const double p = segment(s);
       if (lane == 0) spart[(int64_t)j * nseg + s] = p;
@@ -1018,7 +1101,7 @@ __global__ void __launch_bounds__(kBlock)
   } else {
     __shared__ double quad_part[kWavesPerBlock];
     const int64_t nquad = quads(nseg);
-    const int64_t qd = blockIdx.x;  // one quad per block (grid.x == nquad)
+    const int64_t qd = pt.bx0 + blockIdx.x;  // one quad per block
     const int64_t s = qd * kWavesPerBlock + wave_in_block();
     store_quad_partial(s < nseg ? segment(s) : 0.0, quad_part, spart + (int64_t)j * nquad + qd);
   }
@@ -1036,22 +1119,22 @@ __device__ __forceinline__ float update_one(float x, float v, float mv, float lr
 // sscale_out; otherwise they are read from sscale (the same buffer).
 template <bool FOLD>
 __global__ void __launch_bounds__(kBlock)
-    update_kernel(int64_t words, int64_t L, int n, const uint64_t* __restrict__ sbits,
+    update_kernel(Part pt, int64_t words, int64_t L, int n, const uint64_t* __restrict__ sbits,
                   const float* __restrict__ sscale, float* __restrict__ sscale_out,
                   const double* __restrict__ spart, int64_t scount, const float* __restrict__ v,
                   float* __restrict__ x, float lr, float eps) {
   const int lane = threadIdx.x & 63;
   __shared__ float fss[FOLD ? kMaxWorkersPerLaunch : 1];
   if constexpr (FOLD)
-    fold_scales_in_block(spart, scount, scount, n, L, fss, sscale_out, 1, blockIdx.x == 0);
+    fold_scales_in_block(spart, scount, scount, n, L, fss, sscale_out, 1,
+                         pt.lo == 0 && blockIdx.x == 0);
   auto scale_of = [&](int64_t jj) -> float {
     if constexpr (FOLD) return fss[jj];
     return sscale[jj];
   };
-  const int64_t ngroups = (words + kSegRows - 1) / kSegRows;
   const int64_t nwave = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t rows_per_chunk = L >> 6;
-  for (int64_t gi = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); gi < ngroups;
+  for (int64_t gi = pt.lo + (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); gi < pt.hi;
        gi += nwave) {
     const int64_t r0 = gi * kSegRows;
     const int rows = words - r0 < kSegRows ? (int)(words - r0) : kSegRows;
@@ -1135,6 +1218,81 @@ unsigned grid_for(int64_t items, int64_t per_block, int64_t cap) {
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// Elements of a streaming pass per launch.  On MI355X a pass moves more
+// bytes per second as a sequence of launches of tens of millions of
+// elements than as one launch over billions: a 2^31-element fp32
+// read-modify-write probe ran at 5.8 TB/s as one launch, 6.1 TB/s as 8
+// launches and 6.4 TB/s as 64 launches of 2^25 (512 launches of 2^22 fell to
+// 5.4 TB/s on their gaps).  On the step itself (sizes 2^24 to 2^27 and
+// unsplit, measured on 110M x 8 bf16, 334M x 16, 1.56G x 8 and 340M x 64)
+// launches of 2^26 and 2^27 were best: 4-5 % off the step where one launch
+// covered 5-12 G elements, neutral where launches were already 340M.  The
+// server pass for 32 and 64 workers, whose waves take 4 segments each, lost
+// to tails when cut (1.05 -> 1.17 ms on 340M x 64 at 2^26): it is cut only
+// past kSegPartialLaunchScale times the size.
+constexpr int64_t kLaunchElems = int64_t(1) << 26;
+constexpr int64_t kSegPartialLaunchScale = 16;
+// s.launch_elems (a debug setting) applies to every pass unscaled.
+int64_t per_launch(const State& s, int64_t scale = 1) {
+  return s.launch_elems > 0 ? s.launch_elems : kLaunchElems * scale;
+}
+
+// Issues a pass over `rows` grid rows of `nbx` blocks, each row `row_elems`
+// elements, as launches of about per_launch(s) elements: whole rows grouped,
+// or, for rows of more than that, ranges of a row's blocks.  one(part, grid,
+// t0, t1) makes one launch; the pass's start event goes with its first
+// launch and its end event with its last, so they time the whole pass.
+template <typename F>
+hipError_t launch_parts(const State& s, int rows, int64_t nbx, int64_t row_elems, hipEvent_t t0,
+                        hipEvent_t t1, F one, int64_t scale = 1) {
+  const int64_t elems = per_launch(s, scale);
+  const int64_t total = (int64_t)rows * row_elems;
+  int64_t cuts = 1;      // parts of one row
+  int per_rows = rows;   // rows of one part
+  if (total > elems) {
+    if (row_elems >= elems) {
+      cuts = std::min<int64_t>(nbx, (row_elems + elems - 1) / elems);
+      per_rows = 1;
+    } else {
+      const int64_t parts = (total + elems - 1) / elems;
+      per_rows = (int)((rows + parts - 1) / parts);
+    }
+  }
+  const int64_t bx_per = (nbx + cuts - 1) / cuts;
+  for (int r0 = 0; r0 < rows; r0 += per_rows) {
+    const int nr = std::min(per_rows, rows - r0);
+    for (int64_t b0 = 0; b0 < nbx; b0 += bx_per) {
+      const int64_t nb = std::min(bx_per, nbx - b0);
+      const bool first = r0 == 0 && b0 == 0;
+      const bool last = r0 + nr == rows && b0 + nb == nbx;
+      const hipError_t e = one(Part{b0, r0, 0, 0}, dim3((unsigned)nb, (unsigned)nr),
+                               first ? t0 : nullptr, last ? t1 : nullptr);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+// The same for a pass whose waves stride over `items` work items of
+// `item_elems` elements each, `per_wave` items a wave: ranges [lo, hi) of
+// about per_launch(s) elements, each launched with enough blocks to give
+// every wave per_wave items (at most `cap` blocks).
+template <typename F>
+hipError_t launch_ranges(const State& s, int64_t items, int64_t item_elems, int per_wave,
+                         int64_t cap, hipEvent_t t0, hipEvent_t t1, F one) {
+  const int64_t elems = per_launch(s);
+  const int64_t total = items * item_elems;
+  const int64_t parts = std::max<int64_t>(1, (total + elems - 1) / elems);
+  const int64_t per = std::max<int64_t>(1, (items + parts - 1) / parts);
+  for (int64_t lo = 0;; lo += per) {
+    const int64_t hi = std::min(items, lo + per);
+    const dim3 grid(grid_for(hi - lo, kWavesPerBlock * per_wave, cap));
+    const hipError_t e = one(Part{0, 0, lo, hi}, grid, lo == 0 ? t0 : nullptr,
+                             hi == items ? t1 : nullptr);
+    if (e != hipSuccess || hi == items) return e;
+  }
+}
 
 }  // namespace
 
@@ -1245,58 +1403,56 @@ hipError_t launch_warmup_finish(const State& s, float lr, float bc1, float bc2,
 hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw, bool m_bits,
                               hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const float ob1 = 1.0f - s.beta1;
-  const dim3 grid(grid_for(s.nseg, kWavesPerBlock, kMaxBlocksPerRow), (unsigned)(nw * s.n));
-#define OB_WORK(GT, MB)                                                                        \
-  return launch(worker_kernel<GT, MB>, grid, dim3(kBlock), stream, t0, t1, g, w0, s.d, s.L, s.n, \
-                s.nseg, s.words, (const float*)s.m, (const uint64_t*)s.sbits,                    \
-                (const float*)s.sscale, s.c, (const float*)s.wscale, s.wbits, s.wpart, s.beta1,  \
-                ob1)
-  if (s.grad_bf16) {
-    if (m_bits) OB_WORK(uint16_t, true);
-    OB_WORK(uint16_t, false);
-  }
-  if (m_bits) OB_WORK(float, true);
-  OB_WORK(float, false);
-#undef OB_WORK
+  auto kernel = s.grad_bf16 ? (m_bits ? worker_kernel<uint16_t, true> : worker_kernel<uint16_t, false>)
+                            : (m_bits ? worker_kernel<float, true> : worker_kernel<float, false>);
+  // grid rows: (worker, chunk), one block per quad of the chunk's segments
+  return launch_parts(s, nw * s.n, quads(s.nseg), s.L, t0, t1,
+                      [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
+                        return launch(kernel, grid, dim3(kBlock), stream, a, b, g, w0, pt, s.d,
+                                      s.L, s.n, s.nseg, s.words, (const float*)s.m,
+                                      (const uint64_t*)s.sbits, (const float*)s.sscale, s.c,
+                                      (const float*)s.wscale, s.wbits, s.wpart, s.beta1, ob1);
+                      });
 }
 
 hipError_t launch_zo_local(const State& s, const GradPtrs& g, bool first, bool m_bits, float wk,
                            hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const float ob1 = 1.0f - s.beta1;
-  const dim3 grid(grid_for(s.nseg, kWavesPerBlock, kMaxBlocksPerRow), (unsigned)(s.n * s.n));
-#define OB_ZOL(GT, F, MB)                                                                       \
-  return launch(zo_local_kernel<GT, F, MB>, grid, dim3(kBlock), stream, t0, t1, g, s.d, s.L, s.n, \
-                s.nseg, (const float*)s.m, (const uint64_t*)s.sbits, (const float*)s.sscale,      \
-                s.mloc, s.aloc, s.beta1, ob1, wk)
-  if (s.grad_bf16) {
-    if (!first) OB_ZOL(uint16_t, false, false);
-    if (m_bits) OB_ZOL(uint16_t, true, true);
-    OB_ZOL(uint16_t, true, false);
-  }
-  if (!first) OB_ZOL(float, false, false);
-  if (m_bits) OB_ZOL(float, true, true);
-  OB_ZOL(float, true, false);
-#undef OB_ZOL
+  // FIRST and MBITS: the shared momentum is read only at a period's first
+  // step, and is held as server sign words after the first synchronization
+  auto kernel =
+      s.grad_bf16
+          ? (!first ? zo_local_kernel<uint16_t, false, false>
+                    : m_bits ? zo_local_kernel<uint16_t, true, true>
+                             : zo_local_kernel<uint16_t, true, false>)
+          : (!first ? zo_local_kernel<float, false, false>
+                    : m_bits ? zo_local_kernel<float, true, true> : zo_local_kernel<float, true, false>);
+  return launch_parts(s, s.n * s.n, quads(s.nseg), s.L, t0, t1,
+                      [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
+                        return launch(kernel, grid, dim3(kBlock), stream, a, b, g, pt, s.d, s.L,
+                                      s.n, s.nseg, (const float*)s.m, (const uint64_t*)s.sbits,
+                                      (const float*)s.sscale, s.mloc, s.aloc, s.beta1, ob1, wk);
+                      });
 }
 
 hipError_t launch_zo_sync(const State& s, const GradPtrs& g, bool first, bool m_bits, float wk,
                           hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const float ob1 = 1.0f - s.beta1;
-  const dim3 grid(grid_for(s.nseg, kWavesPerBlock, kMaxBlocksPerRow), (unsigned)(s.n * s.n));
-#define OB_ZOS(GT, F, MB)                                                                      \
-  return launch(zo_sync_kernel<GT, F, MB>, grid, dim3(kBlock), stream, t0, t1, g, s.d, s.L, s.n, \
-                s.nseg, s.words, (const float*)s.m, (const uint64_t*)s.sbits,                    \
-                (const float*)s.sscale, (const float*)s.mloc, (const float*)s.aloc, s.c,         \
-                (const float*)s.wscale, s.wbits, s.wpart, s.beta1, ob1, wk)
-  if (s.grad_bf16) {
-    if (!first) OB_ZOS(uint16_t, false, false);
-    if (m_bits) OB_ZOS(uint16_t, true, true);
-    OB_ZOS(uint16_t, true, false);
-  }
-  if (!first) OB_ZOS(float, false, false);
-  if (m_bits) OB_ZOS(float, true, true);
-  OB_ZOS(float, true, false);
-#undef OB_ZOS
+  auto kernel =
+      s.grad_bf16
+          ? (!first ? zo_sync_kernel<uint16_t, false, false>
+                    : m_bits ? zo_sync_kernel<uint16_t, true, true>
+                             : zo_sync_kernel<uint16_t, true, false>)
+          : (!first ? zo_sync_kernel<float, false, false>
+                    : m_bits ? zo_sync_kernel<float, true, true> : zo_sync_kernel<float, true, false>);
+  return launch_parts(s, s.n * s.n, quads(s.nseg), s.L, t0, t1,
+                      [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
+                        return launch(kernel, grid, dim3(kBlock), stream, a, b, g, pt, s.d, s.L,
+                                      s.n, s.nseg, s.words, (const float*)s.m,
+                                      (const uint64_t*)s.sbits, (const float*)s.sscale,
+                                      (const float*)s.mloc, (const float*)s.aloc, s.c,
+                                      (const float*)s.wscale, s.wbits, s.wpart, s.beta1, ob1, wk);
+                      });
 }
 
 hipError_t launch_zo_refresh(const State& s, const GradPtrs& g, hipStream_t stream,
@@ -1383,50 +1539,65 @@ hipError_t launch_worker_scales(const State& s, hipStream_t stream, hipEvent_t t
                        t0, t1);
 }
 
-hipError_t launch_server_pass(const State& s, bool fold_scales, hipStream_t stream,
-                              hipEvent_t t0, hipEvent_t t1) {
+using ServerKernel = void (*)(Part, int64_t, int, int64_t, int64_t, const uint64_t*,
+                              const float*, float*, const double*, int64_t, float*, const float*,
+                              uint64_t*, double*);
+
+template <int NG, bool WQ>
+ServerKernel server_groups_for(bool fold, bool stage) {
+  if (fold)
+    return stage ? server_groups_kernel<NG, WQ, true, true> : server_groups_kernel<NG, WQ, true, false>;
+  return stage ? server_groups_kernel<NG, WQ, false, true> : server_groups_kernel<NG, WQ, false, false>;
+}
+
+template <int NW>
+ServerKernel server_for(bool fold) {
+  return fold ? server_kernel<NW, true> : server_kernel<NW, false>;
+}
+
+hipError_t launch_server_pass(const State& s, bool fold_scales, bool stage_words,
+                              hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const int64_t wcount = worker_row_partials(s);
+  auto run = [&](ServerKernel k, Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
+    return launch(k, grid, dim3(kBlock), stream, a, b, pt, s.L, s.n, s.nseg, s.words,
+                  (const uint64_t*)s.wbits, (const float*)s.wscale, s.wscale,
+                  (const double*)s.wpart, wcount, s.u, (const float*)s.sscale, s.sbits, s.spart);
+  };
   if (s.n == 8 || s.n == 16 || s.n == 32 || s.n == 64) {
-    // segments per wave (measured): 1 up to 16 workers, 4 beyond (the tables
-    // are built once per block)
-    const int per_wave = s.n <= 16 ? 1 : 4;
-    const dim3 grid(grid_for(s.nseg, kWavesPerBlock * per_wave, kMaxBlocksPerRow), (unsigned)s.n);
-#define OB_SRVG(NG, WQ)                                                                          \
-  return fold_scales                                                                             \
-             ? launch(server_groups_kernel<NG, WQ, true>, grid, dim3(kBlock), stream, t0, t1, s.L, \
-                      s.n, s.nseg, s.words, (const uint64_t*)s.wbits, (const float*)s.wscale,    \
-                      s.wscale, (const double*)s.wpart, wcount, s.u, (const float*)s.sscale,     \
-                      s.sbits, s.spart)                                                          \
-             : launch(server_groups_kernel<NG, WQ, false>, grid, dim3(kBlock), stream, t0, t1,    \
-                      s.L, s.n, s.nseg, s.words, (const uint64_t*)s.wbits,                       \
-                      (const float*)s.wscale, s.wscale, (const double*)s.wpart, wcount, s.u,     \
-                      (const float*)s.sscale, s.sbits, s.spart)
-    switch (s.n) {
-      case 8: OB_SRVG(1, false);
-      case 16: OB_SRVG(2, false);
-      case 32: OB_SRVG(4, server_segment_partials(32));
-      default: OB_SRVG(8, server_segment_partials(64));
-    }
-#undef OB_SRVG
+    // staging in LDS needs 16-byte aligned sign words: an even number of
+    // rows per chunk
+    const bool stage = stage_words && ((s.L >> 6) & 1) == 0;
+    const ServerKernel k = s.n == 8    ? server_groups_for<1, false>(fold_scales, stage)
+                           : s.n == 16 ? server_groups_for<2, false>(fold_scales, stage)
+                           : s.n == 32 ? server_groups_for<4, server_segment_partials(32)>(
+                                             fold_scales, stage)
+                                       : server_groups_for<8, server_segment_partials(64)>(
+                                             fold_scales, stage);
+    if (!server_segment_partials(s.n))  // one quad per block, as the worker pass
+      return launch_parts(s, s.n, quads(s.nseg), s.L, t0, t1,
+                          [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
+                            return run(k, pt, grid, a, b);
+                          });
+    // 32 and 64 workers: waves take 4 segments each of the part's segment
+    // range [lo, hi), strided by the launch (the tables are built once per
+    // block)
+    return launch_parts(s, s.n, s.nseg, s.L, t0, t1,
+                        [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
+                          const Part seg{0, pt.by0, pt.bx0, pt.bx0 + (int64_t)grid.x};
+                          const dim3 g(grid_for(grid.x, kWavesPerBlock * 4, kMaxBlocksPerRow),
+                                       grid.y);
+                          return run(k, seg, g, a, b);
+                        },
+                        kSegPartialLaunchScale);
   }
-  const dim3 grid(grid_for(s.nseg, kWavesPerBlock, kMaxBlocksPerRow), (unsigned)s.n);
-#define OB_SRV(NW)                                                                               \
-  return fold_scales                                                                             \
-             ? launch(server_kernel<NW, true>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n,      \
-                      s.nseg, s.words, (const uint64_t*)s.wbits, (const float*)s.wscale,         \
-                      s.wscale, (const double*)s.wpart, wcount, s.u, (const float*)s.sscale,     \
-                      s.sbits, s.spart)                                                          \
-             : launch(server_kernel<NW, false>, grid, dim3(kBlock), stream, t0, t1, s.L, s.n,     \
-                      s.nseg, s.words, (const uint64_t*)s.wbits, (const float*)s.wscale,         \
-                      s.wscale, (const double*)s.wpart, wcount, s.u, (const float*)s.sscale,     \
-                      s.sbits, s.spart)
-  switch (s.n) {
-    case 1: OB_SRV(1);
-    case 2: OB_SRV(2);
-    case 4: OB_SRV(4);
-    default: OB_SRV(0);
-  }
-#undef OB_SRV
+  const ServerKernel k = s.n == 1   ? server_for<1>(fold_scales)
+                         : s.n == 2 ? server_for<2>(fold_scales)
+                         : s.n == 4 ? server_for<4>(fold_scales)
+                                    : server_for<0>(fold_scales);
+  return launch_parts(s, s.n, quads(s.nseg), s.L, t0, t1,
+                      [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
+                        return run(k, pt, grid, a, b);
+                      });
 }
 
 hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
@@ -1436,12 +1607,16 @@ hipError_t launch_server_scales(const State& s, hipStream_t stream, hipEvent_t t
 
 hipError_t launch_update(const State& s, float lr, bool fold_scales, hipStream_t stream,
                          hipEvent_t t0, hipEvent_t t1) {
-  const int64_t groups = (s.words + kSegRows - 1) / kSegRows;
-  const dim3 grid(grid_for(groups, kWavesPerBlock, kMaxBlocksPerRow));
-  return launch(fold_scales ? update_kernel<true> : update_kernel<false>, grid, dim3(kBlock),
-                stream, t0, t1, s.words, s.L, s.n, (const uint64_t*)s.sbits,
-                (const float*)s.sscale, s.sscale, (const double*)s.spart, server_row_partials(s),
-                (const float*)s.v, s.x, lr, s.eps);
+  const int64_t groups = (s.words + kSegRows - 1) / kSegRows;  // of 16 rows, one wave each
+  auto kernel = fold_scales ? update_kernel<true> : update_kernel<false>;
+  return launch_ranges(s, groups, kSegElems, 1, kMaxBlocksPerRow, t0, t1,
+                       [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
+                         return launch(kernel, grid, dim3(kBlock), stream, a, b, pt, s.words,
+                                       s.L, s.n, (const uint64_t*)s.sbits,
+                                       (const float*)s.sscale, s.sscale,
+                                       (const double*)s.spart, server_row_partials(s),
+                                       (const float*)s.v, s.x, lr, s.eps);
+                       });
 }
 
 hipError_t launch_error_out(const float* comp, const float* scales, int64_t L, int64_t offset,

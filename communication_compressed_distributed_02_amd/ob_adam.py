@@ -188,7 +188,8 @@ def ob_adam_check_guards(h):
     return bad.value
 
 
-OB_DEBUG_SYNC, OB_DEBUG_GUARDS, OB_DEBUG_SEPARATE_SCALES = 1, 2, 4
+(OB_DEBUG_SYNC, OB_DEBUG_GUARDS, OB_DEBUG_SEPARATE_SCALES, OB_DEBUG_UNSTAGED_SERVER,
+ OB_DEBUG_SMALL_LAUNCHES) = 1, 2, 4, 8, 16
 
 
 def ob_adam_set_debug(h, flags):

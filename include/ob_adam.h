@@ -313,10 +313,28 @@ ob_status ob_adam_check_guards(ob_adam_t h, int32_t* first_bad);
  *                    for n <= 16) have them folded inside the server pass
  *                    and the update, in the same order: a step is then three
  *                    dispatches, and OB_K_WORKER_SCALE / OB_K_SERVER_SCALE
- *                    record no launches.
+ *                    record no launches;
+ *  OB_DEBUG_UNSTAGED_SERVER - the server pass for 8, 16, 32 and 64 workers
+ *                    loads every worker's sign words of a segment straight
+ *                    into registers, half a 128-byte line at a time.
+ *                    Without it, chunks of an even number of 64-element rows
+ *                    have each segment's words copied whole into LDS first
+ *                    (gfx950's direct global-to-LDS load), so no line is
+ *                    fetched twice;
+ *  OB_DEBUG_SMALL_LAUNCHES - the streaming passes (worker, 0/1 local and
+ *                    synchronizing, server, update) are issued as launches of
+ *                    about 4096 elements each instead of about 2^26, which
+ *                    exercises how a pass is cut into launches on small
+ *                    shapes.
  * The first two make every call synchronous.  None changes a result bit.
  * OB_ERR_ARG for other flag bits. */
-enum { OB_DEBUG_SYNC = 1, OB_DEBUG_GUARDS = 2, OB_DEBUG_SEPARATE_SCALES = 4 };
+enum {
+  OB_DEBUG_SYNC = 1,
+  OB_DEBUG_GUARDS = 2,
+  OB_DEBUG_SEPARATE_SCALES = 4,
+  OB_DEBUG_UNSTAGED_SERVER = 8,
+  OB_DEBUG_SMALL_LAUNCHES = 16
+};
 ob_status ob_adam_set_debug(ob_adam_t h, int32_t flags);
 
 /* Steps taken so far (warm-up and compressed) and compressed steps taken. */
@@ -335,13 +353,15 @@ enum {
   OB_NUM_KERNELS = 8
 };
 
-/* Per-kernel timing.  With max_launches > 0, each later kernel launch (for a
- * kernel made of several dispatches: from the first to the last) gets a pair
- * of HIP events taken from its dispatch packets on the handle's stream (the
- * runtime's extended launch; no extra packets between kernels), up to
- * max_launches launches (later ones are counted as dropped); 0 turns timing
- * off and releases the events.  The events are host-side runtime objects (no
- * device memory is allocated). */
+/* Per-kernel timing.  With max_launches > 0, each later launch of an OB_K_*
+ * kernel gets a pair of HIP events taken from its dispatch packets on the
+ * handle's stream (the runtime's extended launch; no extra packets between
+ * kernels), up to max_launches launches (later ones are counted as dropped);
+ * 0 turns timing off and releases the events.  A kernel made of several
+ * dispatches -- a streaming pass over more than about 2^26 elements is cut
+ * into launches of that size, a long scale finalize takes two -- is timed
+ * from the start of its first dispatch to the end of its last.  The events
+ * are host-side runtime objects (no device memory is allocated). */
 ob_status ob_adam_set_timing(ob_adam_t h, int32_t max_launches);
 
 /* Synchronize the stream, then return for each kernel (index OB_K_*) the

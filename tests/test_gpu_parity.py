@@ -55,15 +55,25 @@ CASES = [
     ("n1_three_groups", 3072064, 1, True, 1e-3, 1, 2),
     ("n1_65_groups", 67114048, 1, False, 1e-3, 1, 2),
     ("n32_segment_partials_two_groups", 32 * 263232, 32, True, 1e-3, 1, 2),
+    # an even number of rows per chunk: the 8-64-worker server pass stages
+    # each segment's sign words in LDS (full segments and ragged ends of
+    # 2, 4 and 8 rows)
+    ("n64_staged_ragged", 64 * 1152, 64, False, 1e-3, 2, 3),
+    ("n32_staged_ragged_bf16", 32 * 2176, 32, True, 1e-3, 2, 3),
+    ("n16_staged_ragged", 16 * 1536, 16, False, 1e-3, 2, 3),
+    ("n8_staged_ragged_bf16", 8 * 41216, 8, True, 1e-3, 2, 3),
+    ("n64_staged_full_segments", 64 * 4096, 64, True, 1e-3, 1, 3),
 ]
 
 
 def run_case(d, n, bf16, sigma, warm, comp, staged=False, exact=True, check_every=True,
-             staged_warm=False):
+             staged_warm=False, debug=0):
     import torch
-    log("case d=%d n=%d bf16=%s warm=%d comp=%d staged=%s staged_warm=%s"
-        % (d, n, bf16, warm, comp, staged, staged_warm))
+    log("case d=%d n=%d bf16=%s warm=%d comp=%d staged=%s staged_warm=%s debug=%d"
+        % (d, n, bf16, warm, comp, staged, staged_warm, debug))
     opt = ob.OneBitAdam(d, n, ob.OB_GRAD_BF16 if bf16 else ob.OB_GRAD_F32)
+    if debug:
+        ob.ob_adam_set_debug(opt.h, debug)
     orc = oracle.Oracle(d, n)
     for t in range(warm + comp):
         hg = host_grads(d, n, t, sigma=sigma, bf16=bf16)
@@ -102,6 +112,28 @@ def test_parity_small(name, d, n, bf16, sigma, warm, comp):
 
 def test_staged_matches_oracle():
     run_case(4 * 3392, 4, False, 1e-2, 2, 3, staged=True)
+
+
+SMALL_LAUNCHES = ["n3_ragged", "n4_ragged", "n5_generic", "n8_bf16", "n16_short_chunks",
+                  "n64_workers", "n32_workers", "n64_staged_ragged", "n16_staged_ragged",
+                  "n1_256_partials_one_group", "n2_two_groups_ragged"]
+
+
+@pytest.mark.parametrize("name", SMALL_LAUNCHES + ["n32_segment_ranges"])
+def test_parity_small_launches(name):
+    """Every streaming pass cut into launches of one block of 4 segments
+    (OB_DEBUG_SMALL_LAUNCHES): rows of the grid grouped several to a launch,
+    rows cut into ranges of blocks, server segment ranges at 32 and 64
+    workers, update ranges; every step against the oracle."""
+    # n32_segment_ranges: chunks of 3 launches and a ragged fourth, so the
+    # 32-worker server pass takes ranges of a chunk's segments
+    cases = dict({c[0]: c[1:] for c in CASES},
+                 n32_segment_ranges=(32 * 13376, 32, False, 1e-3, 1, 2))
+    run_case(*cases[name], debug=ob.OB_DEBUG_SMALL_LAUNCHES)
+
+
+def test_staged_small_launches_match_oracle():
+    run_case(5 * 9280, 5, True, 1e-3, 2, 3, staged=True, debug=ob.OB_DEBUG_SMALL_LAUNCHES)
 
 
 STAGED_WARM = [

@@ -72,12 +72,15 @@ def compare_local(opt, orc, n, where):
 
 
 @pytest.mark.parametrize("name,d,n,bf16,warm,sched", CASES, ids=[c[0] for c in CASES])
-def test_zero_one_matches_oracle(name, d, n, bf16, warm, sched):
+def test_zero_one_matches_oracle(name, d, n, bf16, warm, sched, debug=0):
     import torch
     plan = SCHEDULES[sched]
-    log("case %s: d=%d n=%d bf16=%s warm=%d schedule=%s" % (name, d, n, bf16, warm, plan))
+    log("case %s: d=%d n=%d bf16=%s warm=%d schedule=%s debug=%d"
+        % (name, d, n, bf16, warm, plan, debug))
     opt = ob.OneBitAdam(d, n, ob.OB_GRAD_BF16 if bf16 else ob.OB_GRAD_F32,
                         method=ob.OB_METHOD_ZERO_ONE)
+    if debug:
+        ob.ob_adam_set_debug(opt.h, debug)
     orc = oracle.Oracle(d, n)
     sigma = 1e-3 if bf16 else 1e-2
     for t in range(warm + len(plan)):
@@ -103,6 +106,14 @@ def test_zero_one_matches_oracle(name, d, n, bf16, warm, sched):
             assert e.value.status == ob.OB_ERR_PHASE
             np.testing.assert_array_equal(gpu_np(opt, ob.OB_X_LOCAL, n - 1), gpu_np(opt, ob.OB_X))
     assert opt.check_guards() == -1, "a kernel wrote past the end of a workspace buffer"
+
+
+@pytest.mark.parametrize("name", ["n4_ragged_pairs", "n8_bf16_irregular", "n64_pairs"])
+def test_zero_one_small_launches(name):
+    """The local and synchronizing passes cut into launches of one block
+    (OB_DEBUG_SMALL_LAUNCHES), against the oracle at every step."""
+    case = {c[0]: c[1:] for c in CASES}[name]
+    test_zero_one_matches_oracle(name, *case, debug=ob.OB_DEBUG_SMALL_LAUNCHES)
 
 
 @pytest.mark.parametrize("n,bf16", [(4, False), (8, True), (3, False)])
