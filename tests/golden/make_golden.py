@@ -43,7 +43,7 @@ from synth import workloads as W  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SAMPLED = {"c1": [0, 1, 2, 3], "c2": list(range(8)), "c3": list(range(16)), "c4": [0, 2, 5, 7],
-           "c5": [0, 3, 7, 11, 15, 19, 23, 27, 31, 35, 39, 43, 47, 51, 55, 59, 63], "idx64": [3],
+           "c5": [0, 7, 15, 23, 31, 39, 47, 55, 63], "idx64": [3],
            "z2": list(range(8)), "z3": list(range(16))}
 N_RANDOM = 2048
 SEG = 1024
