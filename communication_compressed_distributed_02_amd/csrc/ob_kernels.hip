@@ -29,7 +29,7 @@
 //  - The worker grid is non-persistent (one wave per segment, grid.y =
 //    worker x chunk): persistent grids and several segments per wave
 //    measured slower.
-//  - The server pass for 8 to 64 workers looks up sums of 8-worker subtrees
+//  - The server pass for 8 to 64 workers looks up sums of 4-worker subtrees
 //    in LDS tables, indexed by the sign bits that a cross-lane bit transpose
 //    of vector-loaded sign words puts in each lane; for other worker counts
 //    it folds the workers' +-s in worker order into per-row stacks.  Both
@@ -842,49 +842,64 @@ __global__ void __launch_bounds__(kBlock)
 }
 
 // ------------------------------------- server pass, 8 to 64 workers ----
-// n = 8*NG workers.  Workers 8g..8g+7 form an aligned subtree of the
-// pairwise tree, so their sum for one element depends only on their 8 sign
-// bits: each block tabulates, in LDS, the 256 possible subtree sums of every
-// group for its chunk's scales (each entry formed in the pairwise order).
+// n = 8*NG workers.  Workers 4t..4t+3 form an aligned subtree of the
+// pairwise tree, so their sum for one element depends only on their 4 sign
+// bits: each block tabulates, in LDS, the 16 possible subtree sums of every
+// such quad for its chunk's scales (each entry formed in the pairwise
+// order), and the sum of an aligned 8-worker subtree is the sum of its two
+// quads' entries -- the tree's next level.  A lookup's 64 lanes read one
+// 16-entry table: 16 distinct words in 16 distinct banks, so no bank
+// conflict (a table of all 256 sums of 8 workers was looked up at random
+// words: its bank conflicts kept the LDS busy for 75 % of the n = 64 pass).
 // The sign words are read with vector loads: for 8 rows, lane 8r + q loads
 // worker 8g + q's word of row r, and a 64x64 bit transpose across the wave
-// leaves in lane e, byte r, the group's 8 sign bits of element e of row r --
-// a table index.  The NG group sums are then added pairwise.  (The scalar
-// form needs one scalar load of 64 bytes per worker and 8 rows, and scalar
-// loads do not overlap: with many workers it was bound by them.)
-
-// Value of x in lane (lane ^ K).
-template <int K>
-__device__ __forceinline__ uint32_t xor_fetch(uint32_t x, int lane) {
-  if constexpr (K == 1) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
-  } else if constexpr (K == 2) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
-  } else if constexpr (K == 4 || K == 8 || K == 16) {
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (K << 10));  // xor within 32
-  } else {
-    return (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ K) << 2, (int)x);
-  }
-}
+// leaves in lane e, byte r, the 8 sign bits of workers 8g..8g+7 for element
+// e of row r: two table indices.  The NG group sums are then added pairwise.
+// (The scalar form needs one scalar load of 64 bytes per worker and 8 rows,
+// and scalar loads do not overlap: with many workers it was bound by them.)
 
 // One exchange stage of the transpose for one 32-bit half: bit K of the bit
 // position swaps with bit K of the lane.  Lanes with bit K clear keep the
-// positions with bit K clear and take the partner's others shifted up by K;
-// lanes with bit K set keep the positions with bit K set and take the
-// partner's others shifted down by K (as rotations: the wrapped bits fall on
-// kept positions).
+// positions with bit K clear and take the partner's (lane + K) others
+// shifted up by K; lanes with bit K set keep the positions with bit K set and
+// take the partner's (lane - K) others shifted down by K.  Every exchange is
+// a VALU cross-lane operation (none goes through the LDS, which the table
+// lookups keep busy):
+//  - K = 16: gfx950's v_permlane16_swap of x with itself gives, in each lane,
+//    x and its partner's x as the pair (lane with bit 4 clear: (own,
+//    partner); set: (partner, own)); one byte permute with a per-lane
+//    selector assembles the halfwords;
+//  - K = 8: the partner's x by DPP row_ror:8 (lane ^ 8 within a 16-lane row),
+//    one byte permute assembles the bytes;
+//  - K = 4: the partner's x by DPP row_half_mirror then quad_perm [3,2,1,0]
+//    (lane ^ 4), K = 2 and 1 by one quad_perm; rotations and a bit select
+//    assemble the nibbles and bits (as rotations: the wrapped bits fall on
+//    kept positions).
 template <int K>
 __device__ __forceinline__ uint32_t transpose_stage(uint32_t x, int lane) {
-  constexpr uint32_t kHigh = K == 16 ? 0xFFFF0000u
-                             : K == 8 ? 0xFF00FF00u
-                             : K == 4 ? 0xF0F0F0F0u
-                             : K == 2 ? 0xCCCCCCCCu
-                                      : 0xAAAAAAAAu;
   const bool upper = (lane & K) != 0;
-  const uint32_t p = xor_fetch<K>(x, lane);
-  const uint32_t r = __builtin_amdgcn_alignbit(p, p, upper ? K : 32 - K);
-  const uint32_t keep = upper ? kHigh : ~kHigh;
-  return (x & keep) | (r & ~keep);
+  if constexpr (K == 16) {
+    const auto pr = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    // v_perm_b32(s0, s1, sel): selector bytes 0-3 take s1's bytes, 4-7 s0's
+    return __builtin_amdgcn_perm(pr[1], pr[0], upper ? 0x07060302u : 0x05040100u);
+  } else if constexpr (K == 8) {
+    const uint32_t p = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);
+    return __builtin_amdgcn_perm(p, x, upper ? 0x03070105u : 0x06020400u);
+  } else {
+    constexpr uint32_t kHigh = K == 4 ? 0xF0F0F0F0u : K == 2 ? 0xCCCCCCCCu : 0xAAAAAAAAu;
+    uint32_t p;
+    if constexpr (K == 4) {
+      const int m = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+      p = (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);        // quad [3,2,1,0]
+    } else if constexpr (K == 2) {
+      p = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+    } else {
+      p = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+    }
+    const uint32_t r = __builtin_amdgcn_alignbit(p, p, upper ? K : 32 - K);
+    const uint32_t keep = upper ? kHigh : ~kHigh;
+    return (x & keep) | (r & ~keep);
+  }
 }
 
 // 64x64 bit transpose across the wave.  On entry lane L holds row L of the
@@ -892,9 +907,12 @@ __device__ __forceinline__ uint32_t transpose_stage(uint32_t x, int lane) {
 // bit L of (lo, hi) is bit e of row L.  (Every stage swaps one bit of the
 // row index with the same bit of the column index; their order is free.)
 __device__ __forceinline__ void transpose64(uint32_t& lo, uint32_t& hi, int lane) {
-  const uint32_t a = xor_fetch<32>(lo, lane);
-  const uint32_t b = xor_fetch<32>(hi, lane);
-  if (lane < 32) hi = a; else lo = b;
+  // bit 5 of the position is the half: lanes 0..31 take the partner's (lane
+  // + 32) lo as their hi, lanes 32..63 the partner's hi as their lo -- one
+  // v_permlane32_swap (lo's upper 32 lanes trade with hi's lower 32)
+  const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+  lo = sw[0];
+  hi = sw[1];
   lo = transpose_stage<16>(lo, lane);
   hi = transpose_stage<16>(hi, lane);
   lo = transpose_stage<8>(lo, lane);
@@ -932,7 +950,8 @@ __device__ __forceinline__ void server_average_groups(const uint64_t* __restrict
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const uint32_t half = rr < 4 ? lo[g] : hi[g];
-      o[g] = tab[g * 256 + __builtin_amdgcn_ubfe(half, 8 * (rr & 3), 8)];
+      o[g] = tab[32 * g + __builtin_amdgcn_ubfe(half, 8 * (rr & 3), 4)] +
+             tab[32 * g + 16 + __builtin_amdgcn_ubfe(half, 8 * (rr & 3) + 4, 4)];
     }
     avg[rr] = pairwise_sum<NG>(o) / (float)(8 * NG);
   }
@@ -965,7 +984,8 @@ __device__ __forceinline__ void server_average_groups_staged(const uint64_t* st,
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const uint32_t half = rr < 4 ? lo[g] : hi[g];
-      o[g] = tab[g * 256 + __builtin_amdgcn_ubfe(half, 8 * (rr & 3), 8)];
+      o[g] = tab[32 * g + __builtin_amdgcn_ubfe(half, 8 * (rr & 3), 4)] +
+             tab[32 * g + 16 + __builtin_amdgcn_ubfe(half, 8 * (rr & 3) + 4, 4)];
     }
     avg[rr] = pairwise_sum<NG>(o) / (float)(8 * NG);
   }
@@ -1014,7 +1034,7 @@ __global__ void __launch_bounds__(kBlock)
                          int64_t wcount, float* __restrict__ u,
                          const float* __restrict__ sscale_prev, uint64_t* __restrict__ sbits,
                          double* __restrict__ spart) {
-  __shared__ float tab[NG * 256];
+  __shared__ float tab[NG * 32];  // quad t of workers 4t..4t+3: tab[16t + its 4 sign bits]
   __shared__ uint64_t stage[STAGE ? kWavesPerBlock * NG * 128 : 1];
   // the folded worker scales are read only while the tables are built, before
   // the barrier that precedes any staging: with STAGE they share its area
@@ -1027,15 +1047,15 @@ __global__ void __launch_bounds__(kBlock)
   if constexpr (FOLD)
     fold_scales_in_block(wpart + (int64_t)j * wcount, (int64_t)n * wcount, wcount, 8 * NG, L, sws,
                          wscale_out + j, n, pt.lo == 0 && pt.bx0 + blockIdx.x == 0);
-  for (int t = threadIdx.x; t < NG * 256; t += kBlock) {
-    const int g = t >> 8, i = t & 255;
-    float v[8];
+  for (int t = threadIdx.x; t < NG * 32; t += kBlock) {
+    const int qd = t >> 4, i = t & 15;
+    float v[4];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const float sc = FOLD ? sws[8 * g + b] : wscale[(8 * g + b) * n + j];
+    for (int b = 0; b < 4; ++b) {
+      const float sc = FOLD ? sws[4 * qd + b] : wscale[(4 * qd + b) * n + j];
       v[b] = ((i >> b) & 1) ? sc : -sc;
     }
-    tab[t] = pairwise_sum<8>(v);
+    tab[t] = pairwise_sum<4>(v);
   }
   __syncthreads();
   const float sp = sscale_prev[j];

@@ -163,6 +163,21 @@ def test_full_size_against_stored_oracle(name, front_end):
     def chunk(field, rec, worker=0):
         return opt.get(field, worker, rec["chunk"] * L, L)
 
+    # whole-chunk digests go through one pinned host buffer (a pageable copy
+    # plus a bytes copy of every chunk made the 0/1 workloads' per-step
+    # digests of every worker's local momenta take minutes)
+    pinned = torch.empty(L * 4, dtype=torch.uint8, pin_memory=True)
+
+    def host_view(t):
+        nb = t.numel() * t.element_size()
+        pinned[:nb].copy_(t.contiguous().view(torch.uint8))
+        return memoryview(pinned[:nb].numpy())
+
+    def digest_chunk(field, rec, worker=0, h=None):
+        h = h if h is not None else xxhash.xxh64()
+        h.update(host_view(chunk(field, rec, worker)))
+        return h
+
     def sampled(field, rec, worker=0):
         loc = torch.as_tensor(rec["arrays"]["loc"].astype(np.int64), device=dev)
         return chunk(field, rec, worker).index_select(0, loc).cpu().numpy()
@@ -175,17 +190,17 @@ def test_full_size_against_stored_oracle(name, front_end):
                                ("es", ob.OB_E_SERVER)):
                 check_sampled("%s chunk %d %s step %d: %s" % (name, j, tag, t, key),
                               sampled(field, rec), arr["%s_%s" % (tag, key)])
-                got = xxhash.xxh64(chunk(field, rec).cpu().numpy().tobytes()).hexdigest()
+                got = digest_chunk(field, rec).hexdigest()
                 assert got == dig[key], "%s chunk %d %s step %d: %s digest" % (name, j, tag, t, key)
             for k, i in enumerate(rec["error_workers"]):
                 check_sampled("%s chunk %d %s step %d: e_w%d" % (name, j, tag, t, i),
                               sampled(ob.OB_E_WORKER, rec, i), arr["%s_e" % tag][k])
             for i in range(n):
-                got = xxhash.xxh64(chunk(ob.OB_E_WORKER, rec, i).cpu().numpy().tobytes())
+                got = digest_chunk(ob.OB_E_WORKER, rec, i)
                 assert got.hexdigest() == dig["e"][i], \
                     "%s chunk %d %s step %d: e_w%d digest" % (name, j, tag, t, i)
             for i, want in enumerate(dig.get("xl", [])):  # inside a 0/1 local period
-                got = xxhash.xxh64(chunk(ob.OB_X_LOCAL, rec, i).cpu().numpy().tobytes())
+                got = digest_chunk(ob.OB_X_LOCAL, rec, i)
                 assert got.hexdigest() == want, \
                     "%s chunk %d %s step %d: local model of worker %d" % (name, j, tag, t, i)
         log("%s: %s checkpoint (step %d) matches: whole-chunk digests and samples"
@@ -242,7 +257,7 @@ def test_full_size_against_stored_oracle(name, front_end):
                 for key, field in (("mh", ob.OB_M_LOCAL), ("ah", ob.OB_A_LOCAL)):
                     h = xxhash.xxh64()
                     for i in range(n):
-                        h.update(chunk(field, rec, i).cpu().numpy().tobytes())
+                        digest_chunk(field, rec, i, h)
                     assert h.hexdigest() == want[key], "%s step %d chunk %d %s" % (name, t, j, key)
             log("%s step %d/%d (local) ok" % (name, t + 1, w.steps))
             if t == recs[0]["mid_t"]:
