@@ -135,14 +135,16 @@ def _load_record(path, key, workload):
 
 
 def load_traffic(workload):
-    """Counter-measured HBM bytes per worker-pass launch, if they were taken
-    on the current kernel source (else None)."""
+    """Counter-measured HBM bytes per worker pass (the summed counters of its
+    dispatches), if they were taken on the current kernel source (else
+    None)."""
     return _load_record(TRAFFIC_FILE, "traffic_record", workload)
 
 
 def load_trace(workload):
-    """rocprofv3's average duration of a steady-state worker-pass launch, if
-    the trace was taken on the current kernel source (else None)."""
+    """rocprofv3's average duration of a steady-state worker pass (the summed
+    durations of its dispatches), if the trace was taken on the current
+    kernel source (else None)."""
     return _load_record(TRACE_FILE, "trace_record", workload)
 
 
@@ -312,29 +314,43 @@ def copy_calibration(mib):
                       "read": "reads 4n", "write": "writes 4n", "dispatches_each": 3}), flush=True)
 
 
+# elements per dispatch of a streaming pass (the library cuts a pass into
+# dispatches of about this many elements)
+DISPATCH_ELEMS = 1 << 26
+
+
 def stream_ceilings(n, bf16=True, reps=5):
-    """GB/s of the probes over n elements on this device: the worker pass's
-    access mix (bf16 gradients: 6 B read + 4 B written per element; fp32:
-    8 + 4), copy, read-only and write-only, with the step's own wave-row
-    mapping and non-temporal hints; and, for reference, the same mix as a
-    torch elementwise kernel and a runtime device-to-device copy."""
+    """GB/s of the probes over n elements on this device, issued as the
+    library issues a pass: dispatches of about DISPATCH_ELEMS elements.  The
+    worker pass's access mix (bf16 gradients: 6 B read + 4 B written per
+    element; fp32: 8 + 4), copy, read-only and write-only, with the step's own
+    wave-row mapping and non-temporal hints; and, for reference, the same mix
+    as a torch elementwise kernel and a runtime device-to-device copy (one
+    dispatch each)."""
     import torch
     lib = probe_lib()
-    n -= n % 4096
+    parts = max(1, -(-n // DISPATCH_ELEMS))
+    per = max(4096, (n // parts) // 4096 * 4096)
+    n = per * parts
     g = torch.zeros(n, dtype=torch.int16 if bf16 else torch.float32, device="cuda:0")
     c = torch.zeros(n, dtype=torch.float32, device="cuda:0")
     c2 = torch.zeros(n, dtype=torch.float32, device="cuda:0")
-    out = {}
+    out = {"elements": n, "dispatches": parts}
     mix = ("mix", g, c, 10 * n) if bf16 else ("mix32", g, c, 12 * n)
+
+    def sliced(kind, a, b):
+        for i in range(parts):
+            run_probe(lib, kind, a[i * per:(i + 1) * per] if a is not None else None,
+                      b[i * per:(i + 1) * per], per)
     for kind, a, b, nbytes in (mix, ("copy", c, c2, 8 * n),
                                ("read", c, c2, 4 * n), ("write", None, c2, 4 * n)):
         for _ in range(2):
-            run_probe(lib, kind, a, b, n)
+            sliced(kind, a, b)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            run_probe(lib, kind, a, b, n)
+            sliced(kind, a, b)
         e1.record()
         torch.cuda.synchronize()
         out[("mix" if kind == "mix32" else kind) + "_GB_s"] = round(
@@ -465,7 +481,7 @@ def main():
     # Region 2: the same K steps again (the next steps of the run) with the
     # library's per-kernel HIP events, taken from the dispatch packets on its
     # stream; they add ~1.5 % to a step, so they stay out of region 1.
-    ob.ob_adam_set_timing(opt.h, (w.n + 4) * a.steps + 8)  # launches per step: n + 4 at most
+    ob.ob_adam_set_timing(opt.h, (w.n + 4) * a.steps + 8)  # passes per step: n + 4 at most
     f0 = torch.cuda.Event(enable_timing=True)
     f1 = torch.cuda.Event(enable_timing=True)
     f0.record()
@@ -495,10 +511,11 @@ def main():
     wk = kernels["worker"]
     traffic = load_traffic(w.name)
     trace = load_trace(w.name)
-    # the same roofline from rocprofv3's average launch duration in the
-    # committed trace of this kernel code (per launch: bytes of one launch)
-    per_launch = ab["worker"] // (w.n if w.staged else 1)
-    trace_gbs = per_launch / (trace["avg_ns"] * 1e-9) / 1e9 if trace else None
+    # the same roofline from rocprofv3's kernel trace of this kernel code,
+    # committed: a pass's algorithmic bytes over the summed durations of its
+    # dispatches, averaged over the run's steady-state passes
+    per_pass = ab["worker"] // (w.n if w.staged else 1)
+    trace_gbs = per_pass / (trace["avg_ns"] * 1e-9) / 1e9 if trace else None
     if zero_one:
         # mean bytes per step over the timed steps' schedule (local steps,
         # synchronizing steps with their finalizes, server pass and update,
@@ -535,20 +552,23 @@ def main():
                      "kernel": "synchronizing worker pass" if zero_one else "worker pass",
                      "achieved": round(wk["GB_s"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(wk["GB_s"] / HBM_PEAK_GBS, 4),
-                     "frac_source": "HIP events around every worker-pass launch of timing "
-                                    "region 2 (live, this run)",
+                     "frac_source": "HIP events from the start of the first to the end of "
+                                    "the last dispatch of every worker pass of timing region 2 "
+                                    "(live, this run)",
                      "achieved_from_trace": round(trace_gbs, 1) if trace else None,
                      "frac_from_trace": round(trace_gbs / HBM_PEAK_GBS, 4) if trace else None,
-                     "trace_avg_us_per_launch": round(trace["avg_ns"] / 1e3, 2) if trace else None,
+                     "trace_avg_us_per_pass": round(trace["avg_ns"] / 1e3, 2) if trace else None,
+                     "trace_dispatches_per_pass": trace.get("dispatches_per_pass") if trace
+                     else None,
                      "trace_kernel": trace["kernel"] if trace else None,
                      "trace_file": os.path.relpath(TRACE_FILE % w.name, ROOT) if trace else None,
-                     "traffic": traffic["bytes_per_launch"] if traffic else None,
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                                     "copy-calibrated)",
-                     "traffic_fetch": traffic["fetch_bytes_per_launch"] if traffic else None,
-                     "traffic_write": traffic["write_bytes_per_launch"] if traffic else None,
-                     "alg_bytes_per_launch": per_launch,
-                     "launches_per_step": w.n if w.staged else 1},
+                     "traffic": traffic["bytes_per_pass"] if traffic else None,
+                     "traffic_unit": "HBM bytes per worker pass (rocprofv3 FETCH_SIZE + "
+                                     "WRITE_SIZE of its dispatches, copy-calibrated)",
+                     "traffic_fetch": traffic["fetch_bytes_per_pass"] if traffic else None,
+                     "traffic_write": traffic["write_bytes_per_pass"] if traffic else None,
+                     "alg_bytes_per_pass": per_pass,
+                     "passes_per_step": w.n if w.staged else 1},
         "step": {"alg_bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                  "frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "fp32_momentum_bytes": None if zero_one else fp32_momentum_step_bytes(w),
@@ -568,7 +588,8 @@ def main():
     torch.cuda.empty_cache()
     ceil = stream_ceilings(min(w.n * w.d if not w.staged else w.d, 1 << 31), w.bf16)
     ceil["note"] = ("probe kernels with the worker pass's mapping over as many elements as one "
-                    "launch of it (at most 2^31); mix = its %d B read + 4 B written per element; "
+                    "pass of it (at most 2^31), in dispatches of about 2^26 elements as the "
+                    "library issues a pass; mix = its %d B read + 4 B written per element; "
                     "torch_mix = the same mix as torch's c += g, runtime_copy = a device-to-"
                     "device copy" % (6 if w.bf16 else 8))
     ceil["worker_frac_of_mix"] = round(wk["GB_s"] / ceil["mix_GB_s"], 4)

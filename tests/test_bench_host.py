@@ -85,14 +85,14 @@ def test_default_workload_is_the_largest_config():
 def test_traffic_records_are_per_workload_and_kernel_code(tmp_path, monkeypatch):
     sha = bench.kernel_sha()
     rec = {"workload": "c3", "kernel_source_sha": sha, "kernel": "worker pass",
-           "bytes_per_launch": 123, "step_bytes": 456}
+           "bytes_per_pass": 123, "step_bytes": 456}
     (tmp_path / "worker_pass_c3_counters.txt").write_text(
         "summary\ntraffic_record: " + json.dumps(rec) + "\n")
     stale = dict(rec, workload="c4", kernel_source_sha="0" * 16)
     (tmp_path / "worker_pass_c4_counters.txt").write_text(
         "traffic_record: " + json.dumps(stale) + "\n")
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "worker_pass_%s_counters.txt"))
-    assert bench.load_traffic("c3")["bytes_per_launch"] == 123
+    assert bench.load_traffic("c3")["bytes_per_pass"] == 123
     assert bench.load_traffic("c4") is None   # taken on other kernel code
     assert bench.load_traffic("c2") is None   # no record
 
@@ -106,7 +106,7 @@ def test_committed_records_name_their_workload():
         assert len(lines) == 1
         rec = json.loads(lines[0][len("traffic_record: "):])
         assert rec["workload"] == name
-        assert rec["bytes_per_launch"] > 0 and rec["step_bytes"] >= rec["bytes_per_launch"]
+        assert rec["bytes_per_pass"] > 0 and rec["step_bytes"] >= rec["bytes_per_pass"]
 
 
 def test_more_than_one_gpu_is_refused():
