@@ -74,6 +74,40 @@ def alg_bytes(w):
     }
 
 
+# elements per dispatch of a streaming pass; the 32- and 64-worker server pass
+# uses 16 times that
+DISPATCH_ELEMS = 1 << 26
+
+
+def pass_dispatches(rows, nbx, row_elems, elems=DISPATCH_ELEMS):
+    """Dispatches the library issues for a pass over `rows` grid rows of
+    `nbx` blocks, each row `row_elems` elements: whole rows grouped into
+    launches of about `elems` elements, or a longer row cut into ranges of
+    its blocks."""
+    total = rows * row_elems
+    cuts, per_rows = 1, rows
+    if total > elems:
+        if row_elems >= elems:
+            cuts, per_rows = min(nbx, -(-row_elems // elems)), 1
+        else:
+            per_rows = -(-rows // -(-total // elems))
+    bx_per = -(-nbx // cuts)
+    return -(-rows // per_rows) * -(-nbx // bx_per)
+
+
+def dispatches_per_pass(w):
+    """Dispatches of one worker pass, server pass and update of workload w."""
+    nseg = -(-w.L // 1024)
+    nquad = -(-nseg // 4)
+    groups = -(-(w.d // 64) // 16)  # the update's waves: 16 rows each
+    return {
+        "worker": pass_dispatches((1 if w.staged else w.n) * w.n, nquad, w.L),
+        "server": (pass_dispatches(w.n, nseg, w.L, 16 * DISPATCH_ELEMS) if w.n in (32, 64)
+                   else pass_dispatches(w.n, nquad, w.L)),
+        "update": -(-groups // -(-groups // max(1, -(-groups * 1024 // DISPATCH_ELEMS)))),
+    }
+
+
 def zo_alg_bytes(w):
     """The 0/1 Adam workloads: algorithmic bytes per launch of each kernel, a
     schedule with `sync_every` = 2 (every local step opens a period, every
@@ -312,11 +346,6 @@ def copy_calibration(mib):
     torch.cuda.synchronize()
     print(json.dumps({"calibration_bytes": 4 * n, "copy": "reads and writes 4n",
                       "read": "reads 4n", "write": "writes 4n", "dispatches_each": 3}), flush=True)
-
-
-# elements per dispatch of a streaming pass (the library cuts a pass into
-# dispatches of about this many elements)
-DISPATCH_ELEMS = 1 << 26
 
 
 def stream_ceilings(n, bf16=True, reps=5):
@@ -568,7 +597,8 @@ def main():
                      "traffic_fetch": traffic["fetch_bytes_per_pass"] if traffic else None,
                      "traffic_write": traffic["write_bytes_per_pass"] if traffic else None,
                      "alg_bytes_per_pass": per_pass,
-                     "passes_per_step": w.n if w.staged else 1},
+                     "passes_per_step": w.n if w.staged else 1,
+                     "dispatches_per_pass": dispatches_per_pass(w)["worker"]},
         "step": {"alg_bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                  "frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "fp32_momentum_bytes": None if zero_one else fp32_momentum_step_bytes(w),

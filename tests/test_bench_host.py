@@ -135,3 +135,36 @@ def test_zero_one_schedule_and_bytes(name):
     nquad = -(-(-(-w.L // 1024)) // 4)
     assert ab["worker"] == w.n * w.d * (gb + 16) + w.n * w.d // 8 + 8 * w.n * w.n * nquad
     assert ab["zo_refresh"] == w.n * w.d * gb + 8 * w.d
+
+
+def test_profiled_dispatch_counts_follow_the_launch_partition():
+    """The committed kernel traces (rocprofv3 dispatch counts) against
+    bench.dispatches_per_pass, the library's rule for cutting a pass into
+    launches: over a traced run of W + 2S compressed steps (--warmup W,
+    --steps S, both timing regions), the steady worker kernel dispatches
+    (W + 2S - 1) passes (the first step runs the fp32-momentum variant), the
+    server pass and the update W + 2S each."""
+    import re
+    for name in ("c1", "c2", "c3", "c4", "c5"):
+        path = bench.TRACE_FILE % name
+        if not os.path.exists(path):
+            continue
+        text = open(path).read()
+        steps = int(re.search(r"--steps (\d+)", text).group(1))
+        warm = int(re.search(r"--warmup (\d+)", text).group(1))
+        calls = {}
+        for line in text.splitlines():
+            m = re.match(r"(\w+_kernel(?:<[^>]*>)?)\s+(\d+)\s+[\d.]+\s+[\d.]+\s+[\d.]+", line)
+            if m:
+                calls[m.group(1)] = int(m.group(2))
+        w = W.make(name)
+        dpp = bench.dispatches_per_pass(w)
+        per = w.n if w.staged else 1
+        comp = warm + 2 * steps
+        worker = [k for k in calls if k.startswith("worker_kernel") and "true>" in k]
+        server = [k for k in calls if k.startswith("server")]
+        update = [k for k in calls if k.startswith("update_kernel")]
+        assert len(worker) == len(server) == len(update) == 1, (name, sorted(calls))
+        assert calls[worker[0]] == (comp - 1) * per * dpp["worker"], name
+        assert calls[server[0]] == comp * dpp["server"], name
+        assert calls[update[0]] == comp * dpp["update"], name
