@@ -325,7 +325,8 @@ ob_status ob_adam_check_guards(ob_adam_t h, int32_t* first_bad);
  *                    synchronizing, server, update) are issued as launches of
  *                    about 4096 elements each instead of about 2^26, which
  *                    exercises how a pass is cut into launches on small
- *                    shapes.
+ *                    shapes (a large shape would take many thousands of
+ *                    launches a pass).
  * The first two make every call synchronous.  None changes a result bit.
  * OB_ERR_ARG for other flag bits. */
 enum {
