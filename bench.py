@@ -260,6 +260,55 @@ def snapshot_chunk0(opt, w):
             "scale_s": get(ob.OB_SCALE_SERVER, 0, 1).view(np.uint32)[0]}
 
 
+def replica_snapshot(w, warm, steps):
+    """The GPU's chunk-0 state after the CPU sample's own schedule -- `warm`
+    warm-up steps, then `steps` compressed (or 0/1 Adam) steps, on the same
+    gradients, step sizes and 0/1 flags -- run on a fresh full-size handle
+    (for a workload whose sample does not follow the timed run's steps, such
+    as c5's: its 30 warm-up steps would not fit the sample's budget)."""
+    import torch
+
+    import synth
+    from communication_compressed_distributed_02_amd import ob_adam as ob
+    dev = torch.device("cuda:0")
+    gdt = torch.bfloat16 if w.bf16 else torch.float32
+    zero_one = w.method == "zero_one"
+    opt = ob.OneBitAdam(w.d, w.n, ob.OB_GRAD_BF16 if w.bf16 else ob.OB_GRAD_F32, w.beta1,
+                        w.beta2, w.eps, device=dev,
+                        method=ob.OB_METHOD_ZERO_ONE if zero_one else ob.OB_METHOD_ONE_BIT)
+
+    def fill(buf, i, t):
+        synth.fill_gpu(buf, 0, t, i, w.dist, w.sigma)
+        for lo, hi in w.pads:
+            buf[lo:hi].zero_()
+    if w.staged:  # one gradient buffer, regenerated per worker
+        one = torch.empty(w.d, dtype=gdt, device=dev)
+        for t in range(warm + steps):
+            for i in range(w.n):
+                fill(one, i, t)
+                (opt.warmup_worker if t < warm else opt.compress_worker)(i, one)
+            (opt.warmup_finish if t < warm else opt.compressed_finish)(w.lr_at(t))
+    else:
+        full = torch.empty((w.n, w.d), dtype=gdt, device=dev)
+        for t in range(warm + steps):
+            for i in range(w.n):
+                fill(full[i], i, t)
+            g = list(full.unbind(0))
+            if t < warm:
+                opt.warmup_step(g, w.lr_at(t))
+            elif zero_one:  # the flags of the step after the workload's own warm-up
+                opt.zero_one_step(g, w.lr_at(t), *w.zo_flags(w.warmup + t - warm))
+            else:
+                opt.compressed_step(g, w.lr_at(t))
+    torch.cuda.synchronize()
+    snap = snapshot_chunk0(opt, w)
+    snap["gpu_run"] = ("a fresh full-size handle running the sample's %d warm-up + %d %s "
+                       "steps" % (warm, steps, "0/1 Adam" if zero_one else "compressed"))
+    del opt
+    torch.cuda.empty_cache()
+    return snap
+
+
 def compare_chunk0(oracle, o, snap, w):
     """Sign words, scales and the step counter bit-exact; x and the errors
     within 1e-5 relative or 1e-6 absolute (worst ratio of error to the
@@ -280,7 +329,9 @@ def compare_chunk0(oracle, o, snap, w):
         worst[name] = float(np.max(np.abs(g64 - r64) / allowed))
     ratio = max(worst.values())
     return {"against": "oracle", "sample": "chunk 0 (%d elements x %d workers), state after "
-            "step %d" % (w.L, n, o.step), "step_equal": snap["step"] == o.step,
+            "step %d" % (w.L, n, o.step),
+            "gpu_run": snap.get("gpu_run", "the timed run's own untimed steps"),
+            "step_equal": snap["step"] == o.step,
             "sign_words_equal": bool(bits), "scales_equal": bool(scales),
             "fp32_worst_error_over_tolerance": ratio,
             "fp32_worst_field": max(worst, key=worst.get),
@@ -626,6 +677,10 @@ def main():
     result["ceilings"] = ceil
     if not a.no_cpu_baseline:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        if snap is None:
+            # the sample does not follow the timed run: replay its schedule on
+            # the GPU (the timed run's memory is free by now)
+            snap = replica_snapshot(w, *cpu_plan(w, cpu_steps))
         result["cpu_baseline"], result["parity"] = cpu_baseline(w, cpu_steps, snap)
     else:
         result["cpu_baseline"] = None
