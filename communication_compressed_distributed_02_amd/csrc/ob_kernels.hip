@@ -325,16 +325,15 @@ __global__ void __launch_bounds__(kBlock)
 // c = ((b1*m) + ((1-b1)*g)) + e with e = c_prev - (c_prev >= 0 ? s_prev : -s_prev);
 // stores c, the row's sign word and the segment's fp64 sum of squares.
 // grid.y = (worker in launch) * n + chunk; grid.x strides over segments.
-template <typename GT, bool MBITS>
+// bm = b1*m, formed by the caller.
+template <typename GT>
 __device__ __forceinline__ void worker_row(const GT* __restrict__ g, float* __restrict__ c,
-                                           const float* __restrict__ m, uint64_t mword, float ms,
-                                           int64_t k, float sp, float beta1, float ob1,
+                                           float bm, int64_t k, float sp, float ob1,
                                            double& acc, uint64_t& word) {
   const float gv = grad_value(g, k);
   const float cp = ld_stream(c + k);
   const float e = cp - (cp >= 0.0f ? sp : -sp);
-  const float mv = MBITS ? signed_scale(mword, ms) : m[k];
-  const float cv = ((beta1 * mv) + (ob1 * gv)) + e;
+  const float cv = (bm + (ob1 * gv)) + e;
   st_stream(c + k, cv);
   word = __ballot(cv >= 0.0f);
   acc = add_square(acc, cv);
@@ -344,14 +343,15 @@ __device__ __forceinline__ void worker_row(const GT* __restrict__ g, float* __re
 // and their partials are folded in LDS (store_quad_partial), so one fp64
 // partial per block reaches HBM and the finalize folds 4x fewer.  One block
 // per quad (grid.x == quads(nseg)): a grid-stride loop here, never taken
-// twice, held 42-50 VGPRs against 32-37 without it.
-template <typename GT, bool MBITS>
+// twice, held 42-50 VGPRs against 32-37 without it.  The momentum is the
+// server's sign words and scales of the previous step.
+template <typename GT>
 __global__ void __launch_bounds__(kBlock)
     worker_kernel(GradPtrs g, int w0, Part pt, int64_t d, int64_t L, int n, int64_t nseg, int64_t words,
-                  const float* __restrict__ m, const uint64_t* __restrict__ sbits,
-                  const float* __restrict__ sscale, float* __restrict__ cbuf,
-                  const float* __restrict__ wscale, uint64_t* __restrict__ wbits,
-                  double* __restrict__ wpart, float beta1, float ob1) {
+                  const uint64_t* __restrict__ sbits, const float* __restrict__ sscale,
+                  float* __restrict__ cbuf, const float* __restrict__ wscale,
+                  uint64_t* __restrict__ wbits, double* __restrict__ wpart, float beta1,
+                  float ob1) {
   __shared__ double quad_part[kWavesPerBlock];
   const int lane = threadIdx.x & 63;
   const int wv = wave_in_block();
@@ -365,7 +365,7 @@ __global__ void __launch_bounds__(kBlock)
   const int64_t nquad = quads(nseg);
   double* __restrict__ part = wpart + ((int64_t)w * n + j) * nquad;
   const float sp = wscale[w * n + j];  // this worker's scale of chunk j, previous step
-  const float ms = MBITS ? sscale[j] : 0.0f;
+  const float ms = sscale[j];
   {
     const int64_t qd = pt.bx0 + blockIdx.x;  // one quad per block
     const int64_t s = qd * kWavesPerBlock + wv;
@@ -384,17 +384,15 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
         for (int r = 0; r < kSegRows; ++r) {
           uint64_t word;
-          const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
-          worker_row<GT, MBITS>(gp, c, m, mword, ms, base + 64 * r + lane, sp, beta1, ob1, acc,
-                                word);
+          worker_row<GT>(gp, c, beta1 * signed_scale(sbits[wbase + r], ms), base + 64 * r + lane,
+                         sp, ob1, acc, word);
           mine = lane == r ? word : mine;
         }
       } else {
         for (int r = 0; r < rows; ++r) {
           uint64_t word;
-          const uint64_t mword = MBITS ? sbits[wbase + r] : 0;
-          worker_row<GT, MBITS>(gp, c, m, mword, ms, base + 64 * r + lane, sp, beta1, ob1, acc,
-                                word);
+          worker_row<GT>(gp, c, beta1 * signed_scale(sbits[wbase + r], ms), base + 64 * r + lane,
+                         sp, ob1, acc, word);
           mine = lane == r ? word : mine;
         }
       }
@@ -402,6 +400,85 @@ __global__ void __launch_bounds__(kBlock)
       if (lane < rows) bits[wbase + lane] = mine;
     }
     store_quad_partial(acc, quad_part, part + qd);
+  }
+}
+
+// bm[r] = b1 * m[k0 + 64*r] for the rows of a segment, all loads issued
+// before the first use (compile-time indices only, so bm lives in
+// registers).  A ragged segment's missing rows load its last row again
+// (unused) rather than branch per row, which made every load wait for the
+// one before it; a wave past the chunk's end (rows == 0) loads nothing.
+__device__ __forceinline__ void load_bm(float* bm, const float* __restrict__ m, int64_t k0,
+                                        int rows, float beta1) {
+  if (rows == 0) return;
+#pragma unroll
+  for (int r = 0; r < kSegRows; ++r)
+    bm[r] = beta1 * ld_stream(m + k0 + 64 * (r < rows ? r : rows - 1));
+}
+
+// The first compressed step, where the momentum is still the warm-up's fp32
+// m.  A block runs its quad for `wg` consecutive workers of the launch in
+// turn (grid.y = worker group * n + chunk): with wg > 1 a wave reads its
+// segment of m once and keeps b1*m in registers, so m is read once per group
+// instead of once per worker; with wg == 1 (ROW_M) m is read row by row next
+// to g and c, as worker_kernel reads its rows (loading a segment's m first
+// made the one-worker pass about 11 % slower).  Each worker's values, sign
+// words and partials are those of worker_kernel (the same fp32 operations
+// per element, the same order of sums).
+template <typename GT, bool ROW_M>
+__global__ void __launch_bounds__(kBlock)
+    worker_first_kernel(GradPtrs g, int w0, int wg, Part pt, int64_t d, int64_t L, int n,
+                        int64_t nseg, int64_t words, const float* __restrict__ m,
+                        float* __restrict__ cbuf, const float* __restrict__ wscale,
+                        uint64_t* __restrict__ wbits, double* __restrict__ wpart, float beta1,
+                        float ob1) {
+  __shared__ double quad_part[kWavesPerBlock];
+  const int lane = threadIdx.x & 63;
+  const int wv = wave_in_block();
+  const int y = pt.by0 + (int)blockIdx.y;
+  const int wg0 = (y / n) * wg;  // the group's first worker within the launch
+  const int j = y - (y / n) * n;
+  const int64_t nquad = quads(nseg);
+  const int64_t qd = pt.bx0 + blockIdx.x;  // one quad per block
+  const int64_t s = qd * kWavesPerBlock + wv;
+  const bool live = s < nseg;
+  const int64_t q0 = s * kSegElems;
+  const int64_t left = live ? (L - q0) >> 6 : 0;
+  const int rows = left < kSegRows ? (int)left : kSegRows;
+  const int64_t base = (int64_t)j * L + q0;
+  const int64_t wbase = base >> 6;
+  float bm[kSegRows];
+  if (!ROW_M) load_bm(bm, m, base + lane, rows, beta1);
+  auto bm_row = [&](int r) { return ROW_M ? beta1 * m[base + 64 * r + lane] : bm[r]; };
+  for (int wi = wg0; wi < wg0 + wg; ++wi) {
+    const int w = w0 + wi;
+    const GT* __restrict__ gp = (const GT*)g.p[wi];
+    float* __restrict__ c = cbuf + (int64_t)w * d;
+    const float sp = wscale[w * n + j];
+    double acc = 0.0;
+    if (live) {
+      uint64_t mine = 0;
+      if (rows == kSegRows) {
+#pragma unroll
+        for (int r = 0; r < kSegRows; ++r) {
+          uint64_t word;
+          worker_row<GT>(gp, c, bm_row(r), base + 64 * r + lane, sp, ob1, acc, word);
+          mine = lane == r ? word : mine;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < kSegRows; ++r) {
+          if (r < rows) {
+            uint64_t word;
+            worker_row<GT>(gp, c, bm_row(r), base + 64 * r + lane, sp, ob1, acc, word);
+            mine = lane == r ? word : mine;
+          }
+        }
+      }
+      acc = butterfly(acc);
+      if (lane < rows) wbits[(int64_t)w * words + wbase + lane] = mine;
+    }
+    store_quad_partial(acc, quad_part, wpart + ((int64_t)w * n + j) * nquad + qd);
   }
 }
 
@@ -475,6 +552,49 @@ __global__ void __launch_bounds__(kBlock)
                                     beta1, ob1, wk, mi, ai);
       st_stream(mloc + k, mi);
       st_stream(aloc + k, ai);
+    }
+  }
+}
+
+// The first local step after the warm-up, where the shared momentum is still
+// the warm-up's fp32 m: as worker_first_kernel, a wave reads its segment of m
+// once and runs the local step of that segment for the `wg` workers of its
+// group in turn (m_i = a_i = (b1*m) + ((1-b1)*g_i), the same fp32 operations
+// as zo_local_kernel).  grid.y = worker group * n + chunk.
+template <typename GT>
+__global__ void __launch_bounds__(kBlock)
+    zo_local_first_kernel(GradPtrs g, int wg, Part pt, int64_t d, int64_t L, int n,
+                          int64_t nseg, const float* __restrict__ m, float* __restrict__ mlocbuf,
+                          float* __restrict__ alocbuf, float beta1, float ob1) {
+  const int lane = threadIdx.x & 63;
+  const int y = pt.by0 + (int)blockIdx.y;
+  const int wg0 = (y / n) * wg;
+  const int j = y - (y / n) * n;
+  const int64_t s = (pt.bx0 + (int64_t)blockIdx.x) * kWavesPerBlock + wave_in_block();
+  if (s >= nseg) return;
+  const int64_t q0 = s * kSegElems;
+  const int64_t left = (L - q0) >> 6;
+  const int rows = left < kSegRows ? (int)left : kSegRows;
+  const int64_t base = (int64_t)j * L + q0;
+  float bm[kSegRows];
+  load_bm(bm, m, base + lane, rows, beta1);
+  for (int wi = wg0; wi < wg0 + wg; ++wi) {
+    const GT* __restrict__ gp = (const GT*)g.p[wi];
+    float* __restrict__ mloc = mlocbuf + (int64_t)wi * d;
+    float* __restrict__ aloc = alocbuf + (int64_t)wi * d;
+    auto row = [&](int r) {
+      const int64_t k = base + 64 * r + lane;
+      const float mi = bm[r] + (ob1 * grad_value(gp, k));
+      st_stream(mloc + k, mi);
+      st_stream(aloc + k, mi);
+    };
+    if (rows == kSegRows) {
+#pragma unroll
+      for (int r = 0; r < kSegRows; ++r) row(r);
+    } else {
+#pragma unroll
+      for (int r = 0; r < kSegRows; ++r)
+        if (r < rows) row(r);
     }
   }
 }
@@ -1428,33 +1548,67 @@ hipError_t launch_warmup_finish(const State& s, float lr, float bc1, float bc2,
                 s.beta2, ob2, bc1, bc2, lr, s.eps);
 }
 
+// Workers per block of the first-step kernels: all nw of the launch, sharing
+// each segment of m, where the chunks hold enough quads for several rounds
+// of blocks without splitting by worker; else one (on 1M parameters x 4
+// workers, 256 blocks of 4 workers took 20 us against 12 us for 1024 blocks
+// of one).
+constexpr int64_t kShareMinBlocks = 4096;
+int first_group(const State& s, int nw) {
+  return (int64_t)s.n * quads(s.nseg) >= kShareMinBlocks ? nw : 1;
+}
+
 hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw, bool m_bits,
                               hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const float ob1 = 1.0f - s.beta1;
-  auto kernel = s.grad_bf16 ? (m_bits ? worker_kernel<uint16_t, true> : worker_kernel<uint16_t, false>)
-                            : (m_bits ? worker_kernel<float, true> : worker_kernel<float, false>);
+  if (!m_bits) {
+    // grid rows: (worker group, chunk).  Launches are sized by elements of m
+    // (a wave's loop over its group is serial, so a launch needs several
+    // rounds of waves to keep the memory busy)
+    const int wg = first_group(s, nw);
+    auto kernel = wg == 1 ? (s.grad_bf16 ? worker_first_kernel<uint16_t, true>
+                                         : worker_first_kernel<float, true>)
+                          : (s.grad_bf16 ? worker_first_kernel<uint16_t, false>
+                                         : worker_first_kernel<float, false>);
+    return launch_parts(s, nw / wg * s.n, quads(s.nseg), s.L, t0, t1,
+                        [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
+                          return launch(kernel, grid, dim3(kBlock), stream, a, b, g, w0, wg, pt,
+                                        s.d, s.L, s.n, s.nseg, s.words, (const float*)s.m, s.c,
+                                        (const float*)s.wscale, s.wbits, s.wpart, s.beta1, ob1);
+                        });
+  }
+  auto kernel = s.grad_bf16 ? worker_kernel<uint16_t> : worker_kernel<float>;
   // grid rows: (worker, chunk), one block per quad of the chunk's segments
   return launch_parts(s, nw * s.n, quads(s.nseg), s.L, t0, t1,
                       [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
                         return launch(kernel, grid, dim3(kBlock), stream, a, b, g, w0, pt, s.d,
-                                      s.L, s.n, s.nseg, s.words, (const float*)s.m,
-                                      (const uint64_t*)s.sbits, (const float*)s.sscale, s.c,
-                                      (const float*)s.wscale, s.wbits, s.wpart, s.beta1, ob1);
+                                      s.L, s.n, s.nseg, s.words, (const uint64_t*)s.sbits,
+                                      (const float*)s.sscale, s.c, (const float*)s.wscale,
+                                      s.wbits, s.wpart, s.beta1, ob1);
                       });
 }
 
 hipError_t launch_zo_local(const State& s, const GradPtrs& g, bool first, bool m_bits, float wk,
                            hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const float ob1 = 1.0f - s.beta1;
+  if (first && !m_bits) {
+    // grid rows: (worker group, chunk); launches sized by elements of m, as
+    // for worker_first_kernel
+    const int wg = first_group(s, s.n);
+    auto kernel = s.grad_bf16 ? zo_local_first_kernel<uint16_t> : zo_local_first_kernel<float>;
+    return launch_parts(s, s.n / wg * s.n, quads(s.nseg), s.L, t0, t1,
+                        [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
+                          return launch(kernel, grid, dim3(kBlock), stream, a, b, g, wg, pt, s.d,
+                                        s.L, s.n, s.nseg, (const float*)s.m, s.mloc, s.aloc,
+                                        s.beta1, ob1);
+                        });
+  }
   // FIRST and MBITS: the shared momentum is read only at a period's first
   // step, and is held as server sign words after the first synchronization
-  auto kernel =
-      s.grad_bf16
-          ? (!first ? zo_local_kernel<uint16_t, false, false>
-                    : m_bits ? zo_local_kernel<uint16_t, true, true>
-                             : zo_local_kernel<uint16_t, true, false>)
-          : (!first ? zo_local_kernel<float, false, false>
-                    : m_bits ? zo_local_kernel<float, true, true> : zo_local_kernel<float, true, false>);
+  auto kernel = s.grad_bf16 ? (first ? zo_local_kernel<uint16_t, true, true>
+                                     : zo_local_kernel<uint16_t, false, false>)
+                            : (first ? zo_local_kernel<float, true, true>
+                                     : zo_local_kernel<float, false, false>);
   return launch_parts(s, s.n * s.n, quads(s.nseg), s.L, t0, t1,
                       [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
                         return launch(kernel, grid, dim3(kBlock), stream, a, b, g, pt, s.d, s.L,
