@@ -63,6 +63,11 @@ CASES = [
     ("n16_staged_ragged", 16 * 1536, 16, False, 1e-3, 2, 3),
     ("n8_staged_ragged_bf16", 8 * 41216, 8, True, 1e-3, 2, 3),
     ("n64_staged_full_segments", 64 * 4096, 64, True, 1e-3, 1, 3),
+    # at least 4096 blocks of 4 segments over all chunks: the first
+    # compressed step shares each segment of the fp32 momentum among a
+    # block's workers (ragged last segments of 5 rows and of 1 row)
+    ("n4_first_step_shared_m", 4 * 4194624, 4, False, 1e-2, 1, 3),
+    ("n8_first_step_shared_m_bf16", 8 * 2097216, 8, True, 1e-3, 1, 3),
 ]
 
 

@@ -38,6 +38,7 @@ SCHEDULES = {
     "pairs_refresh_doubling": [L, R, L, R, L, S, L, R],
     "triples": [L, L, S, L, L, R, L, L, S],
     "irregular": [L, L, L, R, S, L, S, L, L, L, L, S],
+    "one_period": [L, L, R],
 }
 
 CASES = [
@@ -50,6 +51,10 @@ CASES = [
     ("n16_triples", 16 * 1152, 16, False, 1, "triples"),
     ("n64_pairs", 64 * 1088, 64, False, 1, "pairs_refresh_doubling"),
     ("n8_every_step", 8 * 2112, 8, True, 2, "every_step"),
+    # chunks of 1025 blocks of segments (4 x 1025 >= 4096 blocks): the first
+    # local step shares each segment of the fp32 momentum among a block's
+    # workers; a ragged last segment of one row
+    ("n4_first_local_shared_m", 4 * 4194368, 4, False, 1, "one_period"),
 ]
 
 
