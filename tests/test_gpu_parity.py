@@ -121,7 +121,8 @@ def test_staged_matches_oracle():
 
 SMALL_LAUNCHES = ["n3_ragged", "n4_ragged", "n5_generic", "n8_bf16", "n16_short_chunks",
                   "n64_workers", "n32_workers", "n64_staged_ragged", "n16_staged_ragged",
-                  "n1_256_partials_one_group", "n2_two_groups_ragged"]
+                  "n1_256_partials_one_group", "n2_two_groups_ragged",
+                  "n8_first_step_shared_m_bf16"]
 
 
 @pytest.mark.parametrize("name", SMALL_LAUNCHES + ["n32_segment_ranges"])

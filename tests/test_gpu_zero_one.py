@@ -113,7 +113,8 @@ def test_zero_one_matches_oracle(name, d, n, bf16, warm, sched, debug=0):
     assert opt.check_guards() == -1, "a kernel wrote past the end of a workspace buffer"
 
 
-@pytest.mark.parametrize("name", ["n4_ragged_pairs", "n8_bf16_irregular", "n64_pairs"])
+@pytest.mark.parametrize("name", ["n4_ragged_pairs", "n8_bf16_irregular", "n64_pairs",
+                                  "n4_first_local_shared_m"])
 def test_zero_one_small_launches(name):
     """The local and synchronizing passes cut into launches of one block
     (OB_DEBUG_SMALL_LAUNCHES), against the oracle at every step."""
