@@ -78,8 +78,29 @@ def compare_local(opt, orc, n, where):
 
 @pytest.mark.parametrize("name,d,n,bf16,warm,sched", CASES, ids=[c[0] for c in CASES])
 def test_zero_one_matches_oracle(name, d, n, bf16, warm, sched, debug=0):
+    run_zero_one(name, d, n, bf16, warm, SCHEDULES[sched], debug)
+
+
+def test_zero_one_random_shapes_match_oracle():
+    """Seeded random shapes and schedules: n in 1..64, 1 to 40 rows of 64 per
+    chunk, bf16 or fp32, 1 or 2 warm-up steps, then 3 to 7 steps each a local
+    step, a synchronization or a synchronization with a variance refresh (so
+    a schedule may also open with a synchronization, or synchronize every
+    step); every field bit-identical to the oracle after every step."""
+    import os
+    # OB_ZO_RANDOM_CASES / OB_ZO_RANDOM_SEED widen the sweep for a one-off run
+    rng = np.random.default_rng(int(os.environ.get("OB_ZO_RANDOM_SEED", "2025")))
+    for case in range(int(os.environ.get("OB_ZO_RANDOM_CASES", "24"))):
+        n = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 17, 24, 31, 32, 33, 48, 63, 64]))
+        rows = int(rng.integers(1, 41))
+        bf16 = bool(rng.integers(0, 2))
+        plan = [[L, S, R][int(k)] for k in rng.choice(3, size=int(rng.integers(3, 8)),
+                                                      p=[0.5, 0.3, 0.2])]
+        run_zero_one("random shape %d" % case, n * 64 * rows, n, bf16, 1 + case % 2, plan)
+
+
+def run_zero_one(name, d, n, bf16, warm, plan, debug=0):
     import torch
-    plan = SCHEDULES[sched]
     log("case %s: d=%d n=%d bf16=%s warm=%d schedule=%s debug=%d"
         % (name, d, n, bf16, warm, plan, debug))
     opt = ob.OneBitAdam(d, n, ob.OB_GRAD_BF16 if bf16 else ob.OB_GRAD_F32,
@@ -118,8 +139,8 @@ def test_zero_one_matches_oracle(name, d, n, bf16, warm, sched, debug=0):
 def test_zero_one_small_launches(name):
     """The local and synchronizing passes cut into launches of one block
     (OB_DEBUG_SMALL_LAUNCHES), against the oracle at every step."""
-    case = {c[0]: c[1:] for c in CASES}[name]
-    test_zero_one_matches_oracle(name, *case, debug=ob.OB_DEBUG_SMALL_LAUNCHES)
+    d, n, bf16, warm, sched = {c[0]: c[1:] for c in CASES}[name]
+    run_zero_one(name, d, n, bf16, warm, SCHEDULES[sched], debug=ob.OB_DEBUG_SMALL_LAUNCHES)
 
 
 @pytest.mark.parametrize("n,bf16", [(4, False), (8, True), (3, False)])
