@@ -418,14 +418,12 @@ __device__ __forceinline__ void load_bm(float* bm, const float* __restrict__ m, 
 
 // The first compressed step, where the momentum is still the warm-up's fp32
 // m.  A block runs its quad for `wg` consecutive workers of the launch in
-// turn (grid.y = worker group * n + chunk): with wg > 1 a wave reads its
-// segment of m once and keeps b1*m in registers, so m is read once per group
-// instead of once per worker; with wg == 1 (ROW_M) m is read row by row next
-// to g and c, as worker_kernel reads its rows (loading a segment's m first
-// made the one-worker pass about 11 % slower).  Each worker's values, sign
-// words and partials are those of worker_kernel (the same fp32 operations
-// per element, the same order of sums).
-template <typename GT, bool ROW_M>
+// turn (grid.y = worker group * n + chunk): a wave reads its segment of m
+// once and keeps b1*m in registers, so m is read once per group instead of
+// once per worker.  Each worker's values, sign words and partials are those
+// of worker_kernel (the same fp32 operations per element, the same order of
+// sums).
+template <typename GT>
 __global__ void __launch_bounds__(kBlock)
     worker_first_kernel(GradPtrs g, int w0, int wg, Part pt, int64_t d, int64_t L, int n,
                         int64_t nseg, int64_t words, const float* __restrict__ m,
@@ -448,8 +446,7 @@ __global__ void __launch_bounds__(kBlock)
   const int64_t base = (int64_t)j * L + q0;
   const int64_t wbase = base >> 6;
   float bm[kSegRows];
-  if (!ROW_M) load_bm(bm, m, base + lane, rows, beta1);
-  auto bm_row = [&](int r) { return ROW_M ? beta1 * m[base + 64 * r + lane] : bm[r]; };
+  load_bm(bm, m, base + lane, rows, beta1);
   for (int wi = wg0; wi < wg0 + wg; ++wi) {
     const int w = w0 + wi;
     const GT* __restrict__ gp = (const GT*)g.p[wi];
@@ -462,7 +459,7 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
         for (int r = 0; r < kSegRows; ++r) {
           uint64_t word;
-          worker_row<GT>(gp, c, bm_row(r), base + 64 * r + lane, sp, ob1, acc, word);
+          worker_row<GT>(gp, c, bm[r], base + 64 * r + lane, sp, ob1, acc, word);
           mine = lane == r ? word : mine;
         }
       } else {
@@ -470,7 +467,7 @@ __global__ void __launch_bounds__(kBlock)
         for (int r = 0; r < kSegRows; ++r) {
           if (r < rows) {
             uint64_t word;
-            worker_row<GT>(gp, c, bm_row(r), base + 64 * r + lane, sp, ob1, acc, word);
+            worker_row<GT>(gp, c, bm[r], base + 64 * r + lane, sp, ob1, acc, word);
             mine = lane == r ? word : mine;
           }
         }
@@ -1566,10 +1563,7 @@ hipError_t launch_worker_pass(const State& s, const GradPtrs& g, int w0, int nw,
     // (a wave's loop over its group is serial, so a launch needs several
     // rounds of waves to keep the memory busy)
     const int wg = first_group(s, nw);
-    auto kernel = wg == 1 ? (s.grad_bf16 ? worker_first_kernel<uint16_t, true>
-                                         : worker_first_kernel<float, true>)
-                          : (s.grad_bf16 ? worker_first_kernel<uint16_t, false>
-                                         : worker_first_kernel<float, false>);
+    auto kernel = s.grad_bf16 ? worker_first_kernel<uint16_t> : worker_first_kernel<float>;
     return launch_parts(s, nw / wg * s.n, quads(s.nseg), s.L, t0, t1,
                         [&](Part pt, dim3 grid, hipEvent_t a, hipEvent_t b) {
                           return launch(kernel, grid, dim3(kBlock), stream, a, b, g, w0, wg, pt,
