@@ -367,6 +367,9 @@ def probe_lib():
     if not os.path.exists(PROBE_LIB):
         raise RuntimeError("libob_probe.so is not built: run __graft_entry__.build()")
     lib = ctypes.CDLL(PROBE_LIB)
+    lib.ob_probe_run_sync.restype = ctypes.c_int
+    lib.ob_probe_run_sync.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 4 + [ctypes.c_int64,
+                                                                                ctypes.c_void_p]
     lib.ob_probe_run.restype = ctypes.c_int
     lib.ob_probe_run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                  ctypes.c_void_p]
@@ -399,14 +402,15 @@ def copy_calibration(mib):
                       "read": "reads 4n", "write": "writes 4n", "dispatches_each": 3}), flush=True)
 
 
-def stream_ceilings(n, bf16=True, reps=5):
+def stream_ceilings(n, bf16=True, reps=5, sync=False):
     """GB/s of the probes over n elements on this device, issued as the
     library issues a pass: dispatches of about DISPATCH_ELEMS elements.  The
     worker pass's access mix (bf16 gradients: 6 B read + 4 B written per
     element; fp32: 8 + 4), copy, read-only and write-only, with the step's own
-    wave-row mapping and non-temporal hints; and, for reference, the same mix
-    as a torch elementwise kernel and a runtime device-to-device copy (one
-    dispatch each)."""
+    wave-row mapping and non-temporal hints; with `sync`, the 0/1 Adam
+    synchronizing worker pass's mix too (gradient + 12 B read, 4 B written);
+    and, for reference, the same mix as a torch elementwise kernel and a
+    runtime device-to-device copy (one dispatch each)."""
     import torch
     lib = probe_lib()
     parts = max(1, -(-n // DISPATCH_ELEMS))
@@ -435,6 +439,30 @@ def stream_ceilings(n, bf16=True, reps=5):
         torch.cuda.synchronize()
         out[("mix" if kind == "mix32" else kind) + "_GB_s"] = round(
             nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    if sync:
+        m = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+        a = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+        st = torch.cuda.current_stream().cuda_stream
+
+        def sync_pass():
+            for i in range(parts):
+                sl = slice(i * per, (i + 1) * per)
+                rc = lib.ob_probe_run_sync(1 if bf16 else 0, g[sl].data_ptr(), m[sl].data_ptr(),
+                                           a[sl].data_ptr(), c[sl].data_ptr(), per, st)
+                if rc != 0:
+                    raise RuntimeError("ob_probe_run_sync failed: %d" % rc)
+        for _ in range(2):
+            sync_pass()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            sync_pass()
+        e1.record()
+        torch.cuda.synchronize()
+        nbytes = ((2 if bf16 else 4) + 16) * n
+        out["sync_mix_GB_s"] = round(nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        del m, a
     # the same access mix and a copy as the vendor stack implements them:
     # torch's elementwise c += g (the gradient widened to fp32 on the fly),
     # and the runtime's device-to-device copy
@@ -667,13 +695,19 @@ def main():
     }
     del grads, bound, ring_grads, opt
     torch.cuda.empty_cache()
-    ceil = stream_ceilings(min(w.n * w.d if not w.staged else w.d, 1 << 31), w.bf16)
+    ceil = stream_ceilings(min(w.n * w.d if not w.staged else w.d, 1 << 31), w.bf16,
+                           sync=zero_one)
     ceil["note"] = ("probe kernels with the worker pass's mapping over as many elements as one "
                     "pass of it (at most 2^31), in dispatches of about 2^26 elements as the "
                     "library issues a pass; mix = its %d B read + 4 B written per element; "
                     "torch_mix = the same mix as torch's c += g, runtime_copy = a device-to-"
                     "device copy" % (6 if w.bf16 else 8))
-    ceil["worker_frac_of_mix"] = round(wk["GB_s"] / ceil["mix_GB_s"], 4)
+    if zero_one:
+        ceil["note"] += ("; sync_mix = the synchronizing worker pass's %d B read + 4 B written "
+                         "per element, against which worker_frac_of_mix is taken"
+                         % (14 if w.bf16 else 16))
+    ceil["worker_frac_of_mix"] = round(wk["GB_s"] / ceil["sync_mix_GB_s" if zero_one
+                                                          else "mix_GB_s"], 4)
     result["ceilings"] = ceil
     if not a.no_cpu_baseline:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)

@@ -53,6 +53,33 @@ __global__ void __launch_bounds__(kBlock) mix32_kernel(const float* __restrict__
   for (int r = 0; r < 16; ++r) st_nt(c + base + 64 * r + lane, cv[r] * 0.5f + gv[r]);
 }
 
+// The 0/1 Adam synchronizing worker pass's mix: gradient (GT), local
+// momentum, mean momentum and compensated momentum read, the compensated
+// momentum written (gb + 12 B read + 4 B written per element).
+template <typename GT>
+__device__ __forceinline__ float probe_value(const GT* p, int64_t k);
+template <>
+__device__ __forceinline__ float probe_value(const uint16_t* p, int64_t k) {
+  return __uint_as_float((uint32_t)ld_nt(p + k) << 16);
+}
+template <>
+__device__ __forceinline__ float probe_value(const float* p, int64_t k) {
+  return ld_nt(p + k);
+}
+template <typename GT>
+__global__ void __launch_bounds__(kBlock) sync_mix_kernel(const GT* __restrict__ g,
+                                                          const float* __restrict__ m,
+                                                          const float* __restrict__ a,
+                                                          float* __restrict__ c) {
+  const int lane = threadIdx.x & 63;
+  const int64_t base = wave_base();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t k = base + 64 * r + lane;
+    st_nt(c + k, ((probe_value(g, k) + ld_nt(m + k)) + ld_nt(a + k)) * 0.5f + ld_nt(c + k));
+  }
+}
+
 // 4 bytes read + 4 written per element: a plain copy.
 __global__ void __launch_bounds__(kBlock) copy_kernel(const float* __restrict__ a,
                                                       float* __restrict__ b) {
@@ -106,5 +133,23 @@ extern "C" int ob_probe_run(int kind, const void* a, void* b, int64_t n, void* s
     case 3: write_kernel<<<grid, block, 0, s>>>((float*)b); break;
     case 4: mix32_kernel<<<grid, block, 0, s>>>((const float*)a, (float*)b); break;
   }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// The synchronizing-pass mix over n elements (a positive multiple of 4096):
+// g holds bf16 (bf16 != 0) or fp32 gradients; m, a, c fp32.  Same returns as
+// ob_probe_run.
+extern "C" int ob_probe_run_sync(int bf16, const void* g, const float* m, const float* a,
+                                 float* c, int64_t n, void* stream) {
+  if (n <= 0 || n % 4096 != 0 || g == nullptr || m == nullptr || a == nullptr || c == nullptr)
+    return 1;
+  const int64_t blocks = n / 4096;
+  if (blocks > 0x7fffffff) return 1;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)blocks), block(kBlock);
+  if (bf16)
+    sync_mix_kernel<uint16_t><<<grid, block, 0, s>>>((const uint16_t*)g, m, a, c);
+  else
+    sync_mix_kernel<float><<<grid, block, 0, s>>>((const float*)g, m, a, c);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
